@@ -58,8 +58,9 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 class Model:
     """Drafter weights, upcast to float64 on demand.
 
-    ``keep`` keeps the upcast copies (small shapes); otherwise every use
-    upcasts again so that only one matrix is held in float64 at a time.
+    ``keep`` keeps every upcast copy (small shapes); otherwise the vocabulary
+    tables (embedding, LM head) are upcast again at each use so that at most
+    one of them is held in float64 at a time.
     """
 
     def __init__(self, shape, weights: Dict[str, np.ndarray], keep: Optional[bool] = None):
@@ -74,7 +75,7 @@ class Model:
         if name in self._cache:
             return self._cache[name]
         v = to_f64(self.w[name], self.shape.dtype)
-        if self.keep:
+        if self.keep or name not in ("embed", "lm_head"):
             self._cache[name] = v
         return v
 
@@ -352,6 +353,7 @@ class StepRecord:
     write_start: np.ndarray  # first context row written by the step
     logits: Optional[np.ndarray] = None
     hidden: Optional[np.ndarray] = None
+    block_ids: Optional[np.ndarray] = None
 
 
 class Session:
@@ -361,8 +363,13 @@ class Session:
     block gives K drafts; the stand-in verifier gives the target's tokens;
     tau = accept(...); the tau newly committed positions (the anchor and the
     tau - 1 accepted drafts) are projected into the context; the next anchor
-    is the target's token at block position tau - 1 (the bonus token when
-    all K drafts were accepted), at position ctx_len.
+    (the target's own token after the accepted prefix, at position ctx_len)
+    is the verifier's independent draw ``bonus``, so that it never depends
+    on the drafted tokens.
+
+    ``draft=False`` skips the forward and accepts a dummy draft: tau depends
+    only on the verifier's agreement draws, so the state advances exactly as
+    with the real draft (used to advance long sessions cheaply).
 
     ``n_new_override`` replaces tau as the appended count (used by a test
     that reproduces the "sequence-length inflation" mistake).
@@ -395,11 +402,14 @@ class Session:
         ids[0] = self.anchor[i]
         return ids
 
-    def step(self, n_new_override: Optional[int] = None) -> StepRecord:
+    def step(self, n_new_override: Optional[int] = None, draft: bool = True) -> StepRecord:
         s, wl, syn = self.model.shape, self.wl, self.synth
         K = wl.K
         ids = np.stack([self.block(i) for i in range(len(self.seqs))])
-        out = draft_block(self.model, self.states, ids)
+        if draft:
+            out = draft_block(self.model, self.states, ids)
+        else:
+            out = DraftOut(np.zeros(ids.shape, np.int64), None, None)
         targets = np.empty_like(ids)
         bonus = []
         for i, b in enumerate(self.seqs):
@@ -413,15 +423,15 @@ class Session:
             f = syn.step_features(s, wl.seed, b, self.step_idx, n_new)
             project_ctx(self.model, self.states[i], f)
             self.committed[i] += int(tau[i])
-            t = int(tau[i])
-            self.anchor[i] = int(targets[i, t - 1]) if t - 1 < K else bonus[i]
+            self.anchor[i] = bonus[i]
         self.step_idx += 1
         return StepRecord(draft=out.draft, target=targets, tau=tau,
                           ctx_len=np.array([st.ctx_len for st in self.states], np.int64),
                           cap=np.array([st.cap for st in self.states], np.int64),
                           write_start=write_start,
                           logits=out.logits if self.keep_outputs else None,
-                          hidden=out.hidden if self.keep_outputs else None)
+                          hidden=out.hidden if self.keep_outputs else None,
+                          block_ids=ids)
 
     def violations(self) -> List[str]:
         errs = []

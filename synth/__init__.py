@@ -272,7 +272,8 @@ def first_anchor(seed: int, b: int, vocab: int) -> int:
 class VerifierDraws:
     agree: np.ndarray      # bool [K]: block position i agrees with the draft
     shift: np.ndarray      # int  [K]: offset in [0, V-2] for disagreeing tokens
-    bonus: int             # token following a fully accepted block
+    bonus: int             # the target's own token after the accepted prefix
+                           # (the next anchor), independent of the draft
 
 
 def verifier_draws(seed: int, b: int, step: int, K: int, vocab: int, a: float,
