@@ -1,0 +1,332 @@
+"""Python binding of libdflash.so, the DFlash draft-block path for MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in ``include/dflash.h``.  PyTorch supplies device
+memory (through the allocator callbacks) and streams.  The library is loaded
+on first use; every call raises ImportError if it has not been built.  There
+is no other code path.
+
+Entry points keep the C names:
+  dflash_model_create / Model      repack drafter weights
+  dflash_ctx_create / Context      per-sequence proposer state
+  dflash_project_ctx               (a1)-(a3) project + append + KV injection
+  dflash_draft_block               (a4)-(a9) one non-causal draft forward
+  dflash_accept                    (a10) greedy acceptance
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+
+DFLASH_F32, DFLASH_BF16 = 0, 1
+MAX_BATCH, MAX_K = 256, 1024
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> status {status}: {msg}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("n_feat", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
+                ("dtype", ctypes.c_int)]
+
+
+class _LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("fc", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(_LayerWeights))]
+
+
+_ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
+_FREE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p)
+
+
+class _Allocator(ctypes.Structure):
+    _fields_ = [("alloc", _ALLOC_FN), ("free", _FREE_FN), ("user", ctypes.c_void_p)]
+
+
+EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_model_create",
+           "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
+           "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_accept",
+           "dflash_ctx_query", "dflash_ctx_buffers", "dflash_profile_enable",
+           "dflash_profile_read", "dflash_phase_name")
+NUM_PHASES = 15
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_diffusion_drafting_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "dflash_version": ([], ctypes.c_char_p),
+        "dflash_abi_version": ([], i32),
+        "dflash_last_error": ([], ctypes.c_char_p),
+        "dflash_model_create": ([ctypes.POINTER(_Config), ctypes.POINTER(_Weights),
+                                 ctypes.POINTER(_Allocator), vp, ctypes.POINTER(vp)], ctypes.c_int),
+        "dflash_model_destroy": ([vp], ctypes.c_int),
+        "dflash_model_bytes": ([vp, i64p, i64p, i64p], ctypes.c_int),
+        "dflash_ctx_create": ([vp, i32, i32p, ctypes.POINTER(_Allocator), vp, ctypes.POINTER(vp)],
+                              ctypes.c_int),
+        "dflash_ctx_destroy": ([vp], ctypes.c_int),
+        "dflash_project_ctx": ([vp, vp, i32p, vp, vp], ctypes.c_int),
+        "dflash_draft_block": ([vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
+        "dflash_accept": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+        "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
+        "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                ctypes.POINTER(vp), i32p], ctypes.c_int),
+        "dflash_profile_enable": ([vp, i32], ctypes.c_int),
+        "dflash_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), i64p], ctypes.c_int),
+        "dflash_phase_name": ([i32], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+class _Lib:
+    """Loads libdflash.so on first use (so that the build step can import
+    this package before the library exists); raises ImportError if it is
+    missing."""
+    _cdll = None
+
+    def __getattr__(self, name):
+        if _Lib._cdll is None:
+            _Lib._cdll = _load()
+        return getattr(_Lib._cdll, name)
+
+
+lib = _Lib()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DFlashError(fn, status, lib.dflash_last_error().decode(errors="replace"))
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+class TorchAllocator:
+    """Device allocations served by PyTorch's caching allocator on ``device``."""
+
+    def __init__(self, device: torch.device):
+        self.device = torch.device(device)
+        self.live: Dict[int, torch.Tensor] = {}
+        self._a = _ALLOC_FN(self._alloc)
+        self._f = _FREE_FN(self._free)
+        self.struct = _Allocator(self._a, self._f, None)
+
+    def _alloc(self, n: int, user) -> int:
+        try:
+            t = torch.empty(int(n), dtype=torch.uint8, device=self.device)
+        except Exception:      # out of memory: the library reports DFLASH_E_ALLOC
+            return 0
+        p = t.data_ptr()
+        self.live[p] = t
+        return p
+
+    def _free(self, p: int, user) -> None:
+        self.live.pop(int(p) if p else 0, None)
+
+    @property
+    def bytes(self) -> int:
+        return sum(t.numel() for t in self.live.values())
+
+
+def config_struct(shape) -> _Config:
+    """``shape``: any object with the fields of ``dflash_config`` (dtype "bf16"/"f32")."""
+    return _Config(shape.hidden, shape.n_layers, shape.n_q_heads, shape.n_kv_heads,
+                   shape.head_dim, shape.intermediate, shape.vocab, shape.n_feat,
+                   float(shape.rope_theta), float(shape.rms_eps),
+                   DFLASH_BF16 if shape.dtype == "bf16" else DFLASH_F32)
+
+
+class Model:
+    """dflash_model_create / dflash_model_destroy.
+
+    ``weights``: device tensors keyed ``embed``, ``lm_head``, ``fc``,
+    ``final_norm`` and ``layers.{l}.{attn_norm,wq,wk,wv,wo,mlp_norm,w_gate,
+    w_up,w_down}`` in the model dtype (bf16 may be given as uint16 bits).
+    ``embed`` stays borrowed: this object keeps a reference to it.
+    """
+
+    def __init__(self, shape, weights: Dict[str, torch.Tensor], device="cuda",
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.alloc = TorchAllocator(self.device)
+        self._embed = weights["embed"]
+        L = shape.n_layers
+        keys = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+        layers = (_LayerWeights * max(L, 1))()
+        for l in range(L):
+            for k in keys:
+                setattr(layers[l], k, _ptr(weights[f"layers.{l}.{k}"]))
+        w = _Weights(_ptr(weights["embed"]), _ptr(weights["lm_head"]), _ptr(weights["fc"]),
+                     _ptr(weights["final_norm"]), layers)
+        cfg = config_struct(shape)
+        h = ctypes.c_void_p()
+        _check("dflash_model_create",
+               lib.dflash_model_create(ctypes.byref(cfg), ctypes.byref(w),
+                                       ctypes.byref(self.alloc.struct), _stream(stream),
+                                       ctypes.byref(h)))
+        self.handle = h
+
+    def bytes(self):
+        a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check("dflash_model_bytes", lib.dflash_model_bytes(self.handle, ctypes.byref(a),
+                                                            ctypes.byref(b), ctypes.byref(c)))
+        return {"layers": a.value, "lm_head": b.value, "proj": c.value}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib.dflash_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Context:
+    """dflash_ctx_create / dflash_ctx_destroy: proposer state for ``batch`` sequences."""
+
+    def __init__(self, model: Model, batch: int, init_cap: Optional[Sequence[int]] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.model = model
+        self.batch = batch
+        self.alloc = TorchAllocator(model.device)
+        caps = None
+        if init_cap is not None:
+            caps = (ctypes.c_int32 * batch)(*[int(c) for c in init_cap])
+        h = ctypes.c_void_p()
+        _check("dflash_ctx_create",
+               lib.dflash_ctx_create(model.handle, batch, caps, ctypes.byref(self.alloc.struct),
+                                     _stream(stream), ctypes.byref(h)))
+        self.handle = h
+
+    def query(self):
+        a = (ctypes.c_int32 * self.batch)()
+        b = (ctypes.c_int32 * self.batch)()
+        _check("dflash_ctx_query", lib.dflash_ctx_query(self.handle, a, b))
+        return list(a), list(b)
+
+    def buffers(self, b: int):
+        c, k, v = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        phys = ctypes.c_int32()
+        _check("dflash_ctx_buffers", lib.dflash_ctx_buffers(self.handle, b, ctypes.byref(c),
+                                                            ctypes.byref(k), ctypes.byref(v),
+                                                            ctypes.byref(phys)))
+        return c.value, k.value, v.value, phys.value
+
+    def profile(self, enable: bool) -> None:
+        _check("dflash_profile_enable", lib.dflash_profile_enable(self.handle, 1 if enable else 0))
+
+    def profile_read(self):
+        """{phase name: (total ms, launches)} since the last read."""
+        ms = (ctypes.c_double * NUM_PHASES)()
+        cnt = (ctypes.c_int64 * NUM_PHASES)()
+        _check("dflash_profile_read", lib.dflash_profile_read(self.handle, ms, cnt))
+        return {lib.dflash_phase_name(i).decode(): (ms[i], cnt[i]) for i in range(NUM_PHASES) if cnt[i]}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib.dflash_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dflash_project_ctx(ctx: Context, feats: torch.Tensor, n_new: Sequence[int],
+                       positions: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> None:
+    nn = (ctypes.c_int32 * ctx.batch)(*[int(n) for n in n_new])
+    if positions is not None and positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    _check("dflash_project_ctx",
+           lib.dflash_project_ctx(ctx.handle, _ptr(feats) if feats is not None and feats.numel() else None,
+                                  nn, _ptr(positions), _stream(stream)))
+
+
+def dflash_draft_block(ctx: Context, block_ids: torch.Tensor, K: int, draft_ids: torch.Tensor,
+                       logits: Optional[torch.Tensor] = None, hidden: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> None:
+    for t, dt in ((block_ids, torch.int32), (draft_ids, torch.int32)):
+        if t.dtype != dt or t.numel() != ctx.batch * K:
+            raise ValueError("block_ids / draft_ids must be int32 [batch, K]")
+    if logits is not None and (logits.dtype != torch.float32 or
+                               logits.numel() != ctx.batch * K * ctx.model.shape.vocab):
+        raise ValueError("logits must be float32 [batch, K, vocab]")
+    _check("dflash_draft_block",
+           lib.dflash_draft_block(ctx.handle, _ptr(block_ids), int(K), _ptr(draft_ids),
+                                  _ptr(logits), _ptr(hidden), _stream(stream)))
+
+
+def dflash_accept(draft_ids: torch.Tensor, target_ids: torch.Tensor, batch: int, K: int,
+                  accept_len: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    for t in (draft_ids, target_ids, accept_len):
+        if t.dtype != torch.int32:
+            raise ValueError("int32 tensors expected")
+    if draft_ids.numel() != batch * K or target_ids.numel() != batch * K or accept_len.numel() != batch:
+        raise ValueError("shape mismatch")
+    _check("dflash_accept", lib.dflash_accept(_ptr(draft_ids), _ptr(target_ids), int(batch), int(K),
+                                              _ptr(accept_len), _stream(stream)))
+
+
+def version() -> str:
+    return lib.dflash_version().decode()
+
+
+def weights_to_device(weights: Dict, device="cuda") -> Dict[str, torch.Tensor]:
+    """Host arrays (bf16 bits as uint16, or float32) -> device tensors; tied
+    tables stay one tensor."""
+    out: Dict[str, torch.Tensor] = {}
+    seen: Dict[int, torch.Tensor] = {}
+    for k, v in weights.items():
+        if id(v) in seen:
+            out[k] = seen[id(v)]
+            continue
+        t = torch.from_numpy(v).to(device)
+        seen[id(v)] = t
+        out[k] = t
+    return out

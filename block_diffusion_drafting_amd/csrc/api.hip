@@ -1,0 +1,772 @@
+// C-ABI of the DFlash draft-block path (declared in include/dflash.h):
+// model repacking, proposer state, buffer growth and launch sequencing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_err;
+
+dflash_status fail(dflash_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                 \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(DFLASH_E_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), \
+                  __FILE__, __LINE__);                                                \
+  } while (0)
+
+struct Alloc {
+  dflash_allocator a{};
+  bool custom = false;
+  void* get(size_t n) {
+    if (n == 0) n = 256;
+    if (custom) return a.alloc(n, a.user);
+    void* p = nullptr;
+    if (hipMalloc(&p, n) != hipSuccess) return nullptr;
+    return p;
+  }
+  void put(void* p) {
+    if (!p) return;
+    if (custom)
+      a.free(p, a.user);
+    else
+      (void)hipFree(p);
+  }
+};
+
+int64_t next_pow2(int64_t n) {
+  int64_t c = 1;
+  while (c < n) c <<= 1;
+  return c;
+}
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+struct dflash_model {
+  dflash_config cfg{};
+  int es = 2;   // element size of weights and features
+  int ces = 2;  // element size of the attention operands (fp16 / fp32)
+  Alloc alloc;
+  std::vector<void*> owned;
+  const void* embed = nullptr;
+  float* gains = nullptr;      // [(2L+1)][H]: attn_norm l, mlp_norm l, final
+  double* inv_freq = nullptr;  // [d/2]
+  std::vector<Packed> qkv, o, gu, down;
+  Packed lm, fc, kv;
+  int64_t layer_bytes = 0, lm_bytes = 0, proj_bytes = 0;
+
+  const float* attn_gain(int l) const { return gains + (size_t)(2 * l) * cfg.hidden; }
+  const float* mlp_gain(int l) const { return gains + (size_t)(2 * l + 1) * cfg.hidden; }
+  const float* final_gain() const { return gains + (size_t)(2 * cfg.n_layers) * cfg.hidden; }
+};
+
+struct Buf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+enum Phase {
+  PH_EMBED, PH_QKV, PH_ATTN, PH_O, PH_GU, PH_DOWN, PH_LM, PH_FINAL, PH_FC, PH_KV, PH_GROW, PH_ROWMAP,
+  PH_COMBINE, PH_RESID, PH_FCFIN
+};
+static const char* kPhaseNames[DFLASH_NUM_PHASES] = {
+    "embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head", "finalize", "fc", "kv_inject",
+    "grow", "rowmap", "attn_combine", "resid_norm", "fc_finalize"};
+
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, size_t>> recs;  // (phase, index of start event)
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+  ~Profiler() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+struct dflash_ctx {
+  const dflash_model* m = nullptr;
+  Profiler prof;
+  int B = 0;
+  Alloc alloc;
+  std::vector<DevSeq> seq;  // host mirror (ctx_len, cap, phys, pointers)
+  DevSeq* seq_dev = nullptr;
+  // workspaces
+  Buf x, ssq, q, bk, bvt, keys, part, attn_part, rowmap;
+  Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
+};
+
+namespace {
+
+dflash_status ensure(Alloc& al, Buf& b, size_t bytes) {
+  if (b.bytes >= bytes && b.p) return DFLASH_OK;
+  al.put(b.p);
+  b.p = nullptr;
+  b.bytes = 0;
+  void* p = al.get(bytes);
+  if (!p) return fail(DFLASH_E_ALLOC, "allocation of %zu bytes failed", bytes);
+  b.p = p;
+  b.bytes = bytes;
+  return DFLASH_OK;
+}
+
+// A zero-filled frag-layout activation matrix of at least `mtiles` x `nkb`
+// fragments (a hi/lo pair for bf16 models).
+dflash_status ensure_frag(dflash_ctx* c, Buf& hi, Buf& lo, bool pair, int mtiles, int nkb, hipStream_t s,
+                          Frag& out) {
+  const size_t bytes = (size_t)mtiles * nkb * BLOCK_BYTES;
+  for (int i = 0; i < (pair ? 2 : 1); ++i) {
+    Buf& b = i ? lo : hi;
+    if (b.bytes < bytes || !b.p) {
+      dflash_status st = ensure(c->alloc, b, bytes);
+      if (st) return st;
+      HIP_TRY(launch_fill_u32((unsigned*)b.p, bytes / 4, 0u, s));
+    }
+  }
+  out.hi = (u32x4*)hi.p;
+  out.lo = pair ? (u32x4*)lo.p : nullptr;
+  out.mtiles = mtiles;
+  out.nkb = nkb;
+  return DFLASH_OK;
+}
+
+// Records a start event now and the end event when destroyed (profiling on).
+struct PhaseTimer {
+  dflash_ctx* c;
+  int phase;
+  hipStream_t s;
+  bool active = false;
+  PhaseTimer(dflash_ctx* c_, int ph, hipStream_t s_) : c(c_), phase(ph), s(s_) {
+    if (!c->prof.on) return;
+    hipEvent_t a = c->prof.get();
+    hipEvent_t b = c->prof.get();
+    if (!a || !b) return;
+    c->prof.recs.push_back({phase, c->prof.used - 2});
+    active = hipEventRecord(a, s) == hipSuccess;
+  }
+  ~PhaseTimer() {
+    if (active) (void)hipEventRecord(c->prof.pool[c->prof.recs.back().second + 1], s);
+  }
+};
+
+dflash_status check_config(const dflash_config* c) {
+  if (!c) return fail(DFLASH_E_ARG, "config is NULL");
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "bad dtype %d", (int)c->dtype);
+  if (c->hidden <= 0 || c->hidden % 64) return fail(DFLASH_E_SHAPE, "hidden %d must be a positive multiple of 64", c->hidden);
+  if (c->n_layers < 0 || c->n_layers > 256) return fail(DFLASH_E_SHAPE, "n_layers %d out of range", c->n_layers);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_E_SHAPE, "head_dim %d: 64 or 128 supported", c->head_dim);
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads)
+    return fail(DFLASH_E_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+  if (c->intermediate <= 0 || c->intermediate % 8) return fail(DFLASH_E_SHAPE, "intermediate %d must be a positive multiple of 8", c->intermediate);
+  if (c->vocab <= 0) return fail(DFLASH_E_SHAPE, "vocab %d", c->vocab);
+  if (c->n_feat <= 0 || (int64_t)c->n_feat * c->hidden > (1 << 24)) return fail(DFLASH_E_SHAPE, "n_feat %d", c->n_feat);
+  if (!(c->rope_theta > 1.0) || !(c->rms_eps >= 0.0)) return fail(DFLASH_E_ARG, "rope_theta must be > 1 and rms_eps >= 0");
+  return DFLASH_OK;
+}
+
+// Build a packed matrix from a host table of source-row addresses.
+dflash_status pack(dflash_model* m, const std::vector<uint64_t>& rows, int kd, hipStream_t s, Packed& out) {
+  const int es = m->es;
+  const int kpl = 16 / es;
+  if (kd % kpl) return fail(DFLASH_E_SHAPE, "reduction length %d not a multiple of %d", kd, kpl);
+  const int n_rows = (int)rows.size();
+  const int n_pad = round_up(n_rows, 16);
+  const int nkb = (kd * es + 63) / 64;
+  std::vector<uint64_t> tbl(rows);
+  tbl.resize(n_pad, 0);
+  const size_t bytes = (size_t)(n_pad / 16) * nkb * BLOCK_BYTES;
+  void* dst = m->alloc.get(bytes);
+  if (!dst) return fail(DFLASH_E_ALLOC, "allocation of %zu bytes for packed weights failed", bytes);
+  m->owned.push_back(dst);
+  uint64_t* dtbl = nullptr;
+  HIP_TRY(hipMalloc((void**)&dtbl, tbl.size() * sizeof(uint64_t)));
+  hipError_t e = hipMemcpyAsync(dtbl, tbl.data(), tbl.size() * sizeof(uint64_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = m->cfg.dtype == DFLASH_BF16 ? launch_pack<bf16_t>(dtbl, n_pad, kd, nkb, (uint8_t*)dst, s)
+                                                       : launch_pack<float>(dtbl, n_pad, kd, nkb, (uint8_t*)dst, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(dtbl);
+  if (e != hipSuccess) return fail(DFLASH_E_HIP, "weight packing failed: %s", hipGetErrorString(e));
+  out.w = (const uint8_t*)dst;
+  out.n_rows = n_rows;
+  out.n_tiles = n_pad / 16;
+  out.kd = kd;
+  out.nkb = nkb;
+  return DFLASH_OK;
+}
+
+int64_t packed_bytes(const Packed& p) { return (int64_t)p.n_tiles * p.nkb * BLOCK_BYTES; }
+
+// Rows of one head's W_q or W_k in RoPE pair order: tile t of the head holds
+// pairs 8t..8t+7, row 2q+c of the tile = channel (8t+q) + c*d/2.
+void rope_rows(std::vector<uint64_t>& rows, const uint8_t* w, int head, int d, int row_bytes) {
+  for (int t = 0; t < d / 16; ++t)
+    for (int rr = 0; rr < 16; ++rr) {
+      const int p = 8 * t + rr / 2;
+      const int f = p + (rr % 2) * (d / 2);
+      rows.push_back((uint64_t)(w + (size_t)(head * d + f) * row_bytes));
+    }
+}
+void plain_rows(std::vector<uint64_t>& rows, const uint8_t* w, int n, int row_bytes) {
+  for (int r = 0; r < n; ++r) rows.push_back((uint64_t)(w + (size_t)r * row_bytes));
+}
+
+bool valid_stream_ptrs(const dflash_weights* w, int L) {
+  if (!w || !w->embed || !w->lm_head || !w->fc || !w->final_norm) return false;
+  if (L > 0 && !w->layers) return false;
+  for (int l = 0; l < L; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.mlp_norm || !lw.w_gate ||
+        !lw.w_up || !lw.w_down)
+      return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_version(void) { return "dflash-mi355x 0.1 (gfx950)"; }
+int32_t dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
+                                  const dflash_allocator* alloc, void* stream, dflash_model** out) {
+  if (!out) return fail(DFLASH_E_ARG, "out is NULL");
+  *out = nullptr;
+  dflash_status st = check_config(cfg);
+  if (st) return st;
+  if (!valid_stream_ptrs(w, cfg->n_layers)) return fail(DFLASH_E_ARG, "a weight pointer is NULL");
+  if (alloc && (!alloc->alloc || !alloc->free)) return fail(DFLASH_E_ARG, "allocator callbacks are NULL");
+  hipStream_t s = (hipStream_t)stream;
+  dflash_model* m = new dflash_model();
+  m->cfg = *cfg;
+  m->es = cfg->dtype == DFLASH_BF16 ? 2 : 4;
+  m->ces = m->es;
+  if (alloc) {
+    m->alloc.a = *alloc;
+    m->alloc.custom = true;
+  }
+  m->embed = w->embed;
+  const int H = cfg->hidden, L = cfg->n_layers, d = cfg->head_dim, nq = cfg->n_q_heads,
+            nkv = cfg->n_kv_heads, I = cfg->intermediate, es = m->es;
+  auto cleanup = [&](dflash_status r) {
+    dflash_model_destroy(m);
+    return r;
+  };
+
+  // gains -> fp32, inverse RoPE frequencies
+  m->gains = (float*)m->alloc.get((size_t)(2 * L + 1) * H * sizeof(float));
+  m->inv_freq = (double*)m->alloc.get((size_t)(d / 2) * sizeof(double));
+  if (!m->gains || !m->inv_freq) return cleanup(fail(DFLASH_E_ALLOC, "allocation failed"));
+  m->owned.push_back(m->gains);
+  m->owned.push_back(m->inv_freq);
+  auto conv = [&](const void* src, float* dst) {
+    return cfg->dtype == DFLASH_BF16 ? launch_to_f32<bf16_t>(src, dst, H, s) : launch_to_f32<float>(src, dst, H, s);
+  };
+  for (int l = 0; l < L; ++l) {
+    if (conv(w->layers[l].attn_norm, (float*)m->attn_gain(l)) != hipSuccess ||
+        conv(w->layers[l].mlp_norm, (float*)m->mlp_gain(l)) != hipSuccess)
+      return cleanup(fail(DFLASH_E_HIP, "gain conversion failed"));
+  }
+  if (conv(w->final_norm, (float*)m->final_gain()) != hipSuccess) return cleanup(fail(DFLASH_E_HIP, "gain conversion failed"));
+  {
+    std::vector<double> inv(d / 2);
+    for (int i = 0; i < d / 2; ++i) inv[i] = pow(cfg->rope_theta, -2.0 * i / d);
+    if (hipMemcpyAsync(m->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return cleanup(fail(DFLASH_E_HIP, "upload of RoPE frequencies failed"));
+  }
+
+  const int rowH = H * es;
+  m->qkv.resize(L);
+  m->o.resize(L);
+  m->gu.resize(L);
+  m->down.resize(L);
+  for (int l = 0; l < L; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    std::vector<uint64_t> rows;
+    for (int h = 0; h < nq; ++h) rope_rows(rows, (const uint8_t*)lw.wq, h, d, rowH);
+    for (int g = 0; g < nkv; ++g) rope_rows(rows, (const uint8_t*)lw.wk, g, d, rowH);
+    plain_rows(rows, (const uint8_t*)lw.wv, nkv * d, rowH);
+    if ((st = pack(m, rows, H, s, m->qkv[l]))) return cleanup(st);
+    rows.clear();
+    plain_rows(rows, (const uint8_t*)lw.wo, H, nq * d * es);
+    if ((st = pack(m, rows, nq * d, s, m->o[l]))) return cleanup(st);
+    rows.clear();
+    for (int t = 0; t < I / 8; ++t)
+      for (int rr = 0; rr < 16; ++rr) {
+        const int g4 = rr / 4, j = rr % 4;
+        const int f = 8 * t + 2 * g4 + j / 2;
+        const uint8_t* base = (const uint8_t*)((j % 2 == 0) ? lw.w_gate : lw.w_up);
+        rows.push_back((uint64_t)(base + (size_t)f * rowH));
+      }
+    if ((st = pack(m, rows, H, s, m->gu[l]))) return cleanup(st);
+    rows.clear();
+    plain_rows(rows, (const uint8_t*)lw.w_down, H, I * es);
+    if ((st = pack(m, rows, I, s, m->down[l]))) return cleanup(st);
+    m->layer_bytes += packed_bytes(m->qkv[l]) + packed_bytes(m->o[l]) + packed_bytes(m->gu[l]) +
+                      packed_bytes(m->down[l]);
+  }
+  {
+    std::vector<uint64_t> rows;
+    plain_rows(rows, (const uint8_t*)w->lm_head, cfg->vocab, rowH);
+    if ((st = pack(m, rows, H, s, m->lm))) return cleanup(st);
+    m->lm_bytes = packed_bytes(m->lm);
+    rows.clear();
+    plain_rows(rows, (const uint8_t*)w->fc, H, cfg->n_feat * H * es);
+    if ((st = pack(m, rows, cfg->n_feat * H, s, m->fc))) return cleanup(st);
+    rows.clear();
+    for (int l = 0; l < L; ++l) {
+      for (int g = 0; g < nkv; ++g) rope_rows(rows, (const uint8_t*)w->layers[l].wk, g, d, rowH);
+      plain_rows(rows, (const uint8_t*)w->layers[l].wv, nkv * d, rowH);
+    }
+    if (L > 0) {
+      if ((st = pack(m, rows, H, s, m->kv))) return cleanup(st);
+    }
+    m->proj_bytes = packed_bytes(m->fc) + (L > 0 ? packed_bytes(m->kv) : 0);
+  }
+  *out = m;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_model_destroy(dflash_model* m) {
+  if (!m) return DFLASH_OK;
+  for (void* p : m->owned) m->alloc.put(p);
+  delete m;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_model_bytes(const dflash_model* m, int64_t* layer_bytes, int64_t* lm_head_bytes,
+                                 int64_t* proj_bytes) {
+  if (!m) return fail(DFLASH_E_ARG, "model is NULL");
+  if (layer_bytes) *layer_bytes = m->layer_bytes;
+  if (lm_head_bytes) *lm_head_bytes = m->lm_bytes;
+  if (proj_bytes) *proj_bytes = m->proj_bytes;
+  return DFLASH_OK;
+}
+
+}  // extern "C"
+
+static dflash_status alloc_seq(dflash_ctx* c, int b, int cap, DevSeq& out) {
+  const dflash_model* m = c->m;
+  const int phys = cap < 64 ? 64 : cap;
+  const size_t ces = m->ces;
+  const size_t kvn = (size_t)m->cfg.n_layers * m->cfg.n_kv_heads * phys * m->cfg.head_dim;
+  DevSeq v{};
+  v.ctx_len = c->seq[b].ctx_len;
+  v.cap = cap;
+  v.phys = phys;
+  v.ctxbuf = c->alloc.get((size_t)phys * m->cfg.hidden * sizeof(float));
+  v.k = c->alloc.get(kvn * ces);
+  v.vt = c->alloc.get(kvn * ces);
+  if (!v.ctxbuf || !v.k || !v.vt) {
+    c->alloc.put(v.ctxbuf);
+    c->alloc.put(v.k);
+    c->alloc.put(v.vt);
+    return fail(DFLASH_E_ALLOC, "allocation of context buffers (cap %d) failed", cap);
+  }
+  out = v;
+  return DFLASH_OK;
+}
+
+extern "C" {
+
+dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int32_t* init_cap,
+                                const dflash_allocator* alloc, void* stream, dflash_ctx** out) {
+  if (!out) return fail(DFLASH_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!m) return fail(DFLASH_E_ARG, "model is NULL");
+  if (batch < 1 || batch > DFLASH_MAX_BATCH) return fail(DFLASH_E_ARG, "batch %d out of [1, %d]", batch, DFLASH_MAX_BATCH);
+  if (alloc && (!alloc->alloc || !alloc->free)) return fail(DFLASH_E_ARG, "allocator callbacks are NULL");
+  if (init_cap)
+    for (int b = 0; b < batch; ++b)
+      if (init_cap[b] < 0 || init_cap[b] > (1 << 30) || (init_cap[b] & (init_cap[b] - 1)))
+        return fail(DFLASH_E_ARG, "init_cap[%d] = %d is not a power of two (or 0)", b, init_cap[b]);
+  hipStream_t s = (hipStream_t)stream;
+  dflash_ctx* c = new dflash_ctx();
+  c->m = m;
+  c->B = batch;
+  if (alloc) {
+    c->alloc.a = *alloc;
+    c->alloc.custom = true;
+  }
+  c->seq.assign(batch, DevSeq{});
+  c->seq_dev = (DevSeq*)c->alloc.get(sizeof(DevSeq) * batch);
+  if (!c->seq_dev) {
+    delete c;
+    return fail(DFLASH_E_ALLOC, "allocation failed");
+  }
+  for (int b = 0; b < batch; ++b) {
+    const int cap = init_cap ? init_cap[b] : 0;
+    if (cap > 0) {
+      DevSeq v;
+      dflash_status st = alloc_seq(c, b, cap, v);
+      if (st) {
+        dflash_ctx_destroy(c);
+        return st;
+      }
+      c->seq[b] = v;
+    }
+    if (launch_set_seq(c->seq_dev, b, c->seq[b], s) != hipSuccess) {
+      dflash_ctx_destroy(c);
+      return fail(DFLASH_E_HIP, "descriptor upload failed");
+    }
+  }
+  *out = c;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_ctx_destroy(dflash_ctx* c) {
+  if (!c) return DFLASH_OK;
+  for (DevSeq& v : c->seq) {
+    c->alloc.put(v.ctxbuf);
+    c->alloc.put(v.k);
+    c->alloc.put(v.vt);
+  }
+  c->alloc.put(c->seq_dev);
+  for (Buf* b : {&c->x, &c->ssq, &c->q, &c->bk, &c->bvt, &c->keys, &c->part, &c->attn_part, &c->rowmap,
+                 &c->xg_hi, &c->xg_lo, &c->o_hi, &c->o_lo, &c->act_hi, &c->act_lo, &c->c_hi, &c->c_lo})
+    c->alloc.put(b->p);
+  delete c;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_ctx_query(const dflash_ctx* c, int32_t* ctx_len, int32_t* cap) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  for (int b = 0; b < c->B; ++b) {
+    if (ctx_len) ctx_len[b] = c->seq[b].ctx_len;
+    if (cap) cap[b] = c->seq[b].cap;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_ctx_buffers(const dflash_ctx* c, int32_t b, const void** ctxbuf, const void** k_cache,
+                                 const void** v_cache, int32_t* phys_rows) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (b < 0 || b >= c->B) return fail(DFLASH_E_ARG, "sequence %d out of range", b);
+  if (ctxbuf) *ctxbuf = c->seq[b].ctxbuf;
+  if (k_cache) *k_cache = c->seq[b].k;
+  if (v_cache) *v_cache = c->seq[b].vt;
+  if (phys_rows) *phys_rows = c->seq[b].phys;
+  return DFLASH_OK;
+}
+
+}  // extern "C"
+
+static EpiArgs base_epi(const dflash_ctx* c, int M) {
+  const dflash_model* m = c->m;
+  EpiArgs e{};
+  e.M = M;
+  e.eps = (float)m->cfg.rms_eps;
+  e.nq = m->cfg.n_q_heads;
+  e.nkv = m->cfg.n_kv_heads;
+  e.d = m->cfg.head_dim;
+  e.H = m->cfg.hidden;
+  e.I = m->cfg.intermediate;
+  e.V = m->cfg.vocab;
+  e.L = m->cfg.n_layers;
+  e.seqs = c->seq_dev;
+  e.inv_freq = m->inv_freq;
+  return e;
+}
+
+// One weight product.  X: frag-layout activations, or (Xrow != null) the
+// caller's row-major features.  Returns the plan (for split-K consumers).
+template <typename T>
+static dflash_status run_gemm(dflash_ctx* c, int phase, int epi, const Packed& W, const Frag& X,
+                              const void* Xrow, int ldx, int M, EpiArgs e, hipStream_t s,
+                              GemmPlan* plan_out = nullptr) {
+  GemmPlan p = plan_gemm(epi, W, M, sizeof(T) == 2, Xrow != nullptr);
+  dflash_status st;
+  if (p.part_floats && (st = ensure(c->alloc, c->part, p.part_floats * sizeof(float)))) return st;
+  GemmArgs g{};
+  g.W = W;
+  g.X = X;
+  g.Xrow = Xrow;
+  g.ldx = ldx;
+  g.M = M;
+  e.part = (float*)c->part.p;
+  e.part_ntiles = W.n_tiles;
+  e.part_mtiles = (M + 15) / 16;
+  {
+    PhaseTimer tm(c, phase, s);
+    HIP_TRY(launch_gemm<T>(epi, p, g, e, s));
+  }
+  if (plan_out) *plan_out = p;
+  return DFLASH_OK;
+}
+
+template <typename T>
+static dflash_status project_impl(dflash_ctx* c, const void* feats, const int32_t* n_new,
+                                  const int32_t* positions, hipStream_t s) {
+  const dflash_model* m = c->m;
+  const int B = c->B, H = m->cfg.hidden;
+  std::vector<int32_t> start(B + 1, 0);
+  for (int b = 0; b < B; ++b) start[b + 1] = start[b] + n_new[b];
+  const int total = start[B];
+  // growth (host-authoritative; enqueued before anything reads the buffers)
+  for (int b = 0; b < B; ++b) {
+    DevSeq& v = c->seq[b];
+    const int64_t need = (int64_t)v.ctx_len + n_new[b];
+    if (n_new[b] == 0 || need <= v.cap) continue;
+    const int cap = (int)next_pow2(need);
+    DevSeq nv;
+    dflash_status st = alloc_seq(c, b, cap, nv);
+    if (st) return st;
+    if (v.ctxbuf) {
+      PhaseTimer tm(c, PH_GROW, s);
+      hipError_t e = launch_grow_copy<typename CacheOf<T>::type>(v, nv, m->cfg.n_layers, m->cfg.n_kv_heads,
+                                                                m->cfg.head_dim, H, s);
+      if (e != hipSuccess) return fail(DFLASH_E_HIP, "growth copy failed: %s", hipGetErrorString(e));
+    }
+    HIP_TRY(launch_set_seq(c->seq_dev, b, nv, s));
+    c->alloc.put(v.ctxbuf);
+    c->alloc.put(v.k);
+    c->alloc.put(v.vt);
+    v = nv;
+  }
+  if (total == 0) return DFLASH_OK;
+  dflash_status st;
+  const int mtiles = (total + 15) / 16;
+  Frag cb;
+  if ((st = ensure(c->alloc, c->rowmap, sizeof(RowMap) * total)) ||
+      (st = ensure_frag(c, c->c_hi, c->c_lo, sizeof(T) == 2, mtiles, m->fc.n_tiles * 16 * m->es / 64, s, cb)))
+    return st;
+  {
+    PhaseTimer tm(c, PH_ROWMAP, s);
+    HIP_TRY(launch_rowmap(start.data(), B, total, positions, c->seq_dev, (RowMap*)c->rowmap.p, s));
+  }
+  EpiArgs e = base_epi(c, total);
+  e.cbuf = cb;
+  e.rowmap = (const RowMap*)c->rowmap.p;
+  const Frag none{};
+  if (mtiles <= 4) {
+    // few rows: split the reduction over workgroups, then add the splits
+    GemmPlan p;
+    if ((st = run_gemm<T>(c, PH_FC, EPI_PART, m->fc, none, feats, m->cfg.n_feat * H, total, e, s, &p))) return st;
+    PhaseTimer tm(c, PH_FCFIN, s);
+    HIP_TRY(launch_fc_finalize<T>((const float*)c->part.p, p.nsplit, mtiles, total, H, e.rowmap, c->seq_dev, cb, s));
+  } else {
+    if ((st = run_gemm<T>(c, PH_FC, EPI_FC, m->fc, none, feats, m->cfg.n_feat * H, total, e, s))) return st;
+  }
+  if (m->cfg.n_layers > 0)
+    if ((st = run_gemm<T>(c, PH_KV, EPI_KV, m->kv, cb, nullptr, 0, total, e, s))) return st;
+  for (int b = 0; b < B; ++b) c->seq[b].ctx_len += n_new[b];
+  return DFLASH_OK;
+}
+
+extern "C" {
+
+dflash_status dflash_project_ctx(dflash_ctx* c, const void* feats, const int32_t* n_new,
+                                 const int32_t* positions, void* stream) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!n_new) return fail(DFLASH_E_ARG, "n_new is NULL");
+  int64_t total = 0;
+  for (int b = 0; b < c->B; ++b) {
+    if (n_new[b] < 0) return fail(DFLASH_E_ARG, "n_new[%d] = %d is negative", b, n_new[b]);
+    if ((int64_t)c->seq[b].ctx_len + n_new[b] > (1 << 30))
+      return fail(DFLASH_E_SHAPE, "sequence %d would exceed 2^30 positions", b);
+    total += n_new[b];
+  }
+  if (total > (1 << 30)) return fail(DFLASH_E_SHAPE, "too many rows in one call");
+  if (total > 0 && !feats) return fail(DFLASH_E_ARG, "feats is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  return c->m->cfg.dtype == DFLASH_BF16 ? project_impl<bf16_t>(c, feats, n_new, positions, s)
+                                        : project_impl<float>(c, feats, n_new, positions, s);
+}
+
+}  // extern "C"
+
+template <typename T>
+static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_t* draft, float* logits,
+                                void* hidden, hipStream_t s) {
+  using CT = typename CacheOf<T>::type;
+  const dflash_model* m = c->m;
+  const dflash_config& cf = m->cfg;
+  const int B = c->B, M = B * K, H = cf.hidden, L = cf.n_layers, d = cf.head_dim;
+  const int nq = cf.n_q_heads, nkv = cf.n_kv_heads, I = cf.intermediate;
+  const int Kpad = round_up(K, 64), G = H / 64, mtiles = (M + 15) / 16;
+  const int ces = m->ces;
+  const bool pair = sizeof(T) == 2;
+  dflash_status st;
+  Frag xg, of, af;
+  if ((st = ensure(c->alloc, c->x, (size_t)M * H * 4)) || (st = ensure(c->alloc, c->ssq, (size_t)G * M * 4)) ||
+      (st = ensure(c->alloc, c->q, (size_t)M * nq * d * ces)) ||
+      (st = ensure(c->alloc, c->bk, (size_t)B * nkv * Kpad * d * ces)) ||
+      (st = ensure(c->alloc, c->bvt, (size_t)B * nkv * Kpad * d * ces)) ||
+      (st = ensure(c->alloc, c->keys, (size_t)M * 8)) ||
+      (st = ensure_frag(c, c->xg_hi, c->xg_lo, pair, mtiles, H * m->es / 64, s, xg)) ||
+      (st = ensure_frag(c, c->o_hi, c->o_lo, pair, mtiles, nq * d * m->es / 64, s, of)) ||
+      (st = ensure_frag(c, c->act_hi, c->act_lo, pair, mtiles, (I * m->es + 63) / 64, s, af)))
+    return st;
+  // attention plan from the host mirror of the context lengths
+  const int rep = nq / nkv;
+  const int qtiles = (K * rep + 15) / 16;
+  const int qgroups = (qtiles + 3) / 4;
+  int64_t work = 0;
+  int max_len = 0;
+  for (int b = 0; b < B; ++b) {
+    work += (int64_t)(c->seq[b].ctx_len + K) * nkv * qgroups;
+    max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
+  }
+  // keys per split: a multiple of 64, at least 256 (several chunks per
+  // workgroup), larger when there is enough work for ~512 workgroups
+  int chunk = 64 * (int)((work + 64 * 512 - 1) / (64 * 512));
+  if (chunk < 256) chunk = 256;
+  const int max_splits = (max_len + chunk - 1) / chunk + (K + chunk - 1) / chunk;
+  if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d) * sizeof(float))))
+    return st;
+
+  {
+    PhaseTimer tm(c, PH_EMBED, s);
+    HIP_TRY(launch_embed<T>(ids, m->embed, L > 0 ? m->attn_gain(0) : m->final_gain(), M, H, cf.vocab,
+                            (float*)c->x.p, xg, (float*)c->ssq.p, (unsigned long long*)c->keys.p, s));
+  }
+  EpiArgs e = base_epi(c, M);
+  e.Kblk = K;
+  e.Kpad = Kpad;
+  e.ssq = (const float*)c->ssq.p;
+  e.ssq_groups = G;
+  e.norm_dim = H;
+  e.q = c->q.p;
+  e.bk = c->bk.p;
+  e.bvt = c->bvt.p;
+  e.act = af;
+  e.logits = logits;
+  e.keys = (unsigned long long*)c->keys.p;
+
+  AttnArgs a{};
+  a.q = c->q.p;
+  a.bk = c->bk.p;
+  a.bvt = c->bvt.p;
+  a.seqs = c->seq_dev;
+  a.part = (float*)c->attn_part.p;
+  a.B = B;
+  a.K = K;
+  a.Kpad = Kpad;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.d = d;
+  a.qgroups = qgroups;
+  a.chunk = chunk;
+  a.max_splits = max_splits;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+
+  const Frag none{};
+  for (int l = 0; l < L; ++l) {
+    if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], xg, nullptr, 0, M, e, s))) return st;
+    a.layer = l;
+    {
+      PhaseTimer tm(c, PH_ATTN, s);
+      HIP_TRY(launch_attention<CT>(a, s));
+    }
+    {
+      PhaseTimer tm(c, PH_COMBINE, s);
+      HIP_TRY((launch_attn_combine<CT, T>(a, of, s)));
+    }
+    GemmPlan p;
+    if ((st = run_gemm<T>(c, PH_O, EPI_PART, m->o[l], of, nullptr, 0, M, e, s, &p))) return st;
+    {
+      PhaseTimer tm(c, PH_RESID, s);
+      HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
+                                   m->mlp_gain(l), xg, (float*)c->ssq.p, s));
+    }
+    if ((st = run_gemm<T>(c, PH_GU, EPI_SWIGLU, m->gu[l], xg, nullptr, 0, M, e, s))) return st;
+    if ((st = run_gemm<T>(c, PH_DOWN, EPI_PART, m->down[l], af, nullptr, 0, M, e, s, &p))) return st;
+    {
+      PhaseTimer tm(c, PH_RESID, s);
+      HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
+                                   l + 1 < L ? m->attn_gain(l + 1) : m->final_gain(), xg, (float*)c->ssq.p, s));
+    }
+  }
+  (void)none;
+  if ((st = run_gemm<T>(c, PH_LM, EPI_ARGMAX, m->lm, xg, nullptr, 0, M, e, s))) return st;
+  {
+    PhaseTimer tm(c, PH_FINAL, s);
+    HIP_TRY(launch_finalize<T>((const unsigned long long*)c->keys.p, M, draft, (const float*)c->x.p,
+                               (const float*)c->ssq.p, G, m->final_gain(), H, (float)cf.rms_eps, hidden, s));
+  }
+  return DFLASH_OK;
+}
+
+extern "C" {
+
+dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* block_ids, int32_t K, int32_t* draft_ids,
+                                 float* logits, void* hidden, void* stream) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!block_ids || !draft_ids) return fail(DFLASH_E_ARG, "block_ids / draft_ids is NULL");
+  if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
+  hipStream_t s = (hipStream_t)stream;
+  return c->m->cfg.dtype == DFLASH_BF16 ? draft_impl<bf16_t>(c, block_ids, K, draft_ids, logits, hidden, s)
+                                        : draft_impl<float>(c, block_ids, K, draft_ids, logits, hidden, s);
+}
+
+dflash_status dflash_profile_enable(dflash_ctx* c, int32_t enable) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  c->prof.on = enable != 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_read(dflash_ctx* c, double* ms, int64_t* count) {
+  if (!c || !ms || !count) return fail(DFLASH_E_ARG, "NULL pointer");
+  for (int i = 0; i < DFLASH_NUM_PHASES; ++i) {
+    ms[i] = 0.0;
+    count[i] = 0;
+  }
+  Profiler& p = c->prof;
+  if (!p.recs.empty()) HIP_TRY(hipEventSynchronize(p.pool[p.recs.back().second + 1]));
+  for (auto& r : p.recs) {
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, p.pool[r.second], p.pool[r.second + 1]));
+    ms[r.first] += t;
+    count[r.first] += 1;
+  }
+  p.recs.clear();
+  p.used = 0;
+  return DFLASH_OK;
+}
+
+const char* dflash_phase_name(int32_t phase) {
+  if (phase < 0 || phase >= DFLASH_NUM_PHASES) return "";
+  return kPhaseNames[phase];
+}
+
+dflash_status dflash_accept(const int32_t* draft_ids, const int32_t* target_ids, int32_t batch, int32_t K,
+                            int32_t* accept_len, void* stream) {
+  if (!draft_ids || !target_ids || !accept_len) return fail(DFLASH_E_ARG, "NULL pointer");
+  if (batch < 1 || batch > (1 << 20)) return fail(DFLASH_E_ARG, "batch = %d out of range", batch);
+  if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
+  HIP_TRY(launch_accept(draft_ids, target_ids, batch, K, accept_len, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

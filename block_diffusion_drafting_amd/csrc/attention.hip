@@ -1,0 +1,343 @@
+// Bidirectional GQA attention of the draft block over [context KV || block KV].
+//
+// The block is denoised in one non-causal forward (kongchang.com "D-Flash",
+// "System architecture"; Google Developers Blog, "Dual cache for
+// attention"): every block row attends to every committed context position
+// of its sequence and to every block row, with no mask.  Context K/V come
+// from the sequence's static cache, block K/V from this layer's QKV
+// epilogue.
+//
+// Work unit (one 256-thread workgroup): sequence b, KV head g, a group of up
+// to four 16-row query tiles (rows = block position x query head sharing g),
+// and one split of the key range (its partial result goes to a buffer that
+// attn_combine merges in split order).  A split is a run of 64-key chunks;
+// each chunk is staged in LDS once (K row-major, V transposed, padded rows
+// against bank conflicts) and read by all four waves, and the global loads
+// of the next chunk are in flight while the current one is computed.  S^T = K Q^T and O^T += V^T P^T run on MFMA; the
+// softmax is online per wave in fp32 (exp2 with the log2(e) folded into
+// the scale).  For bf16 the two 16-key S^T tiles of a 32-key step hold keys
+// in the order that makes each lane's probabilities the B-fragment of the
+// P.V product directly.
+//
+// T is the attention operand type: fp16 for bf16 models (queries, keys,
+// values and probabilities), fp32 for fp32 models.  The output is fp32.
+#include "kernels.h"
+
+namespace dflash {
+
+// Keys per LDS chunk (two chunks are resident): 64, or 32 for fp32 operands
+// with head_dim 128.
+template <typename T, int D>
+constexpr int chunk_keys() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
+
+size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d) {
+  // per wave: O^T [d][16] + m[16] + l[16]
+  return (size_t)B * nkv * qgroups * max_splits * 4 * (d * 16 + 32);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+  using E = Elem<T>;
+  constexpr int CHUNK_KEYS = chunk_keys<T, D>();
+  constexpr int ES = sizeof(T);
+  constexpr int KROW = D * ES + 16;           // padded LDS row of K (bytes)
+  constexpr int VROW = CHUNK_KEYS * ES + 16;  // padded LDS row of V^T (bytes)
+  constexpr int NFD = D * ES / 64;            // 16-byte fragments along d per lane
+  constexpr int NDT = D / 16;                 // 16-row tiles of d
+  constexpr int KP = 4 * E::KPL;              // keys per P.V step (32 bf16, 16 fp32)
+  constexpr int KP_ROW = D * ES / 16;                   // 16-byte pieces per K row
+  constexpr int KPIECES = CHUNK_KEYS * KP_ROW;
+  constexpr int VP_ROW = CHUNK_KEYS * ES / 16;          // 16-byte pieces per V^T row
+  constexpr int VPIECES = D * VP_ROW;
+  constexpr int EPP = 16 / ES;                          // keys per V^T piece
+  constexpr int KPT = KPIECES / 256, VPT = VPIECES / 256;
+  static_assert(KPIECES % 256 == 0 && VPIECES % 256 == 0, "chunk staging");
+  __shared__ __attribute__((aligned(16))) uint8_t kl[2][CHUNK_KEYS * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t vl[2][D * VROW];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, col = lane & 15;
+  int u = blockIdx.x;
+  const int s = u % a.max_splits;
+  u /= a.max_splits;
+  const int qg = u % a.qgroups;
+  u /= a.qgroups;
+  const int g = u % a.nkv;
+  const int b = u / a.nkv;
+
+  const DevSeq sq = a.seqs[b];
+  const int ctx_len = sq.ctx_len;
+  const int n_cs = (ctx_len + a.chunk - 1) / a.chunk;
+  const int n_bs = (a.K + a.chunk - 1) / a.chunk;
+  const int n_s = n_cs + n_bs;
+  if (s >= n_s) return;
+
+  const T* kbase;
+  const T* vbase;
+  int vstride, k0, k1;
+  if (s < n_cs) {
+    kbase = (const T*)sq.k + ((size_t)a.layer * a.nkv + g) * sq.phys * D;
+    vbase = (const T*)sq.vt + ((size_t)a.layer * a.nkv + g) * D * sq.phys;
+    vstride = sq.phys;
+    k0 = s * a.chunk;
+    k1 = min(ctx_len, k0 + a.chunk);
+  } else {
+    kbase = (const T*)a.bk + ((size_t)b * a.nkv + g) * a.Kpad * D;
+    vbase = (const T*)a.bvt + ((size_t)b * a.nkv + g) * D * a.Kpad;
+    vstride = a.Kpad;
+    k0 = (s - n_cs) * a.chunk;
+    k1 = min(a.K, k0 + a.chunk);
+  }
+
+  // query rows of this wave: r = qtile*16 + col -> head h, block row i
+  const int rep = a.nq / a.nkv;
+  const int nrows = a.K * rep;
+  const int qt = qg * 4 + wave;
+  const int r = qt * 16 + col;
+  const bool row_ok = r < nrows;
+  const int h = g * rep + (row_ok ? r / a.K : 0);
+  const int i = row_ok ? r % a.K : 0;
+  u32x4 qf[NFD];
+  {
+    const T* qp = (const T*)a.q + ((size_t)(b * a.K + i) * a.nq + h) * D;
+#pragma unroll
+    for (int f = 0; f < NFD; ++f)
+      qf[f] = row_ok ? gld16(qp + f * E::KB + g4 * E::KPL) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x4 o[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Chunk staging through registers: the global loads of chunk c+1 are in
+  // flight while chunk c is computed from LDS.  Keys at or past the split
+  // end load as zero (K rows and V^T columns).
+  u32x4 kr[KPT], vr[VPT];
+  auto gload = [&](int c0, int cend) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int t = threadIdx.x + j * 256;
+      const int row = t / KP_ROW, pc = t % KP_ROW;
+      kr[j] = (c0 + row < cend) ? gld16((const uint8_t*)(kbase + (size_t)(c0 + row) * D) + pc * 16)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int t = threadIdx.x + j * 256;
+      const int dr = t / VP_ROW, pc = t % VP_ROW;
+      const int key = c0 + pc * EPP;
+      const T* src = vbase + (size_t)dr * vstride + key;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (key + EPP <= cend) {
+        v = gld16(src);
+      } else if (key < cend) {
+        T tmp[EPP];
+#pragma unroll
+        for (int e2 = 0; e2 < EPP; ++e2) tmp[e2] = (key + e2 < cend) ? gld(src + e2) : (T)0;
+        v = *(const u32x4*)tmp;
+      }
+      vr[j] = v;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int t = threadIdx.x + j * 256;
+      *(u32x4*)(kl[buf] + (t / KP_ROW) * KROW + (t % KP_ROW) * 16) = kr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int t = threadIdx.x + j * 256;
+      *(u32x4*)(vl[buf] + (t / VP_ROW) * VROW + (t % VP_ROW) * 16) = vr[j];
+    }
+  };
+
+  const int nchunks = (k1 - k0 + CHUNK_KEYS - 1) / CHUNK_KEYS;
+  gload(k0, min(k1, k0 + CHUNK_KEYS));
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int c0 = k0 + c * CHUNK_KEYS;
+    const int cend = min(k1, c0 + CHUNK_KEYS);
+    const int buf = c & 1;
+    if (c + 1 < nchunks) gload(c0 + CHUNK_KEYS, min(k1, c0 + 2 * CHUNK_KEYS));
+    const uint8_t* klb = kl[buf];
+    const uint8_t* vlb = vl[buf];
+
+#pragma unroll
+    for (int sub = 0; sub < CHUNK_KEYS / KP; ++sub) {
+      const int kb = sub * KP;  // key offset of this P.V step within the chunk
+      float sv[8];
+      int nv;
+      if constexpr (ES == 2) {
+        // two S^T tiles: tile A rows -> keys 8*(row/4) + row%4, tile B -> +4
+        const int rowA = kb + ((col >> 2) << 3) + (col & 3);
+        const int rowB = rowA + 4;
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < NFD; ++f) {
+          const u32x4 ka = *(const u32x4*)(klb + rowA * KROW + f * 64 + g4 * 16);
+          const u32x4 kb2 = *(const u32x4*)(klb + rowB * KROW + f * 64 + g4 * 16);
+          sa = E::mma(ka, qf[f], sa);
+          sb = E::mma(kb2, qf[f], sb);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sv[j] = sa[j];
+          sv[4 + j] = sb[j];
+        }
+        nv = 8;
+      } else {
+        const int row = kb + col;
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < NFD; ++f) {
+          const u32x4 ka = *(const u32x4*)(klb + row * KROW + f * 64 + g4 * 16);
+          sa = E::mma(ka, qf[f], sa);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[j] = sa[j];
+        nv = 4;
+      }
+      // lane holds keys c0 + kb + g4*nv + j for query column `col`
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < nv) {
+          const int key = c0 + kb + g4 * nv + j;
+          sv[j] = (key < cend) ? sv[j] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[j]);
+        }
+      }
+      mx = wave_xor_max16_32(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_safe);
+      float pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < nv) {
+          pv[j] = exp2f(sv[j] - m_safe);
+          psum += pv[j];
+        }
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+      const u32x4 pf = f_to_frag<T>(pv);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        const u32x4 vf = *(const u32x4*)(vlb + (t * 16 + col) * VROW + kb * ES + g4 * 16);
+        o[t] = E::mma(vf, pf, o[t]);
+      }
+    }
+    if (c + 1 < nchunks) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  l_run = wave_xor_sum16_32(l_run);
+
+  // o[t][j] = O^T[d = 16t + 4*g4 + j][query column col]; every split writes
+  // its partial (m, l, O); attn_combine merges them in split order.
+  const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
+  const size_t wstride = (size_t)D * 16 + 32;
+  float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) *(f32x4*)(pp + (t * 64 + lane) * 4) = o[t];
+  if (g4 == 0) {
+    pp[D * 16 + col] = m_run;
+    pp[D * 16 + 16 + col] = l_run;
+  }
+}
+
+// One workgroup per (sequence, KV head, query group, 16-row d-tile); wave w
+// merges query tile 4*qg + w over the splits in index order and writes its
+// part of o (frag layout of the model type T over nq*d, input of the output
+// projection).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, Frag out) {
+  constexpr int NDT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, col = lane & 15;
+  int u = blockIdx.x;
+  const int t = u % NDT;
+  u /= NDT;
+  const int qg = u % a.qgroups;
+  u /= a.qgroups;
+  const int g = u % a.nkv;
+  const int b = u / a.nkv;
+  const int ctx_len = a.seqs[b].ctx_len;
+  const int n_s = (ctx_len + a.chunk - 1) / a.chunk + (a.K + a.chunk - 1) / a.chunk;
+  const int rep = a.nq / a.nkv;
+  const int r = (qg * 4 + wave) * 16 + col;
+  if (r >= a.K * rep) return;
+  const int h = g * rep + r / a.K, i = r % a.K;
+  const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
+  const size_t wstride = (size_t)D * 16 + 32;
+  const float* base = a.part + (unit * a.max_splits * 4 + wave) * wstride;
+  const size_t sstride = 4 * wstride;   // next split, same wave
+  // online merge in split order; loads are issued eight splits at a time
+  float M = -INFINITY, L = 0.f;
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_s; s0 += 8) {
+    float ms[8], ls[8];
+    f32x4 os[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < n_s) {
+        const float* pp = base + (s0 + k) * sstride;
+        ms[k] = pp[D * 16 + col];
+        ls[k] = pp[D * 16 + 16 + col];
+        os[k] = *(const f32x4*)(pp + (t * 64 + lane) * 4);
+      } else {
+        ms[k] = -INFINITY;
+        ls[k] = 0.f;
+        os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (ms[k] == -INFINITY) continue;
+      const float Mn = fmaxf(M, ms[k]);
+      const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+      const float a1 = exp2f(ms[k] - Mn);
+      L = L * a0 + ls[k] * a1;
+      o = o * a0 + os[k] * a1;
+      M = Mn;
+    }
+  }
+  const float inv = 1.f / L;
+  float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  frag_store<T, 4>(out, b * a.K + i, h * D + t * 16 + g4 * 4, v);
+}
+
+template <typename T>
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)a.B * a.nkv * a.qgroups * a.max_splits);
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((attention_kernel<T, 64>), grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((attention_kernel<T, 128>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_attention<f16_t>(const AttnArgs&, hipStream_t);
+template hipError_t launch_attention<float>(const AttnArgs&, hipStream_t);
+
+template <typename CT, typename T>
+hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s) {
+  dim3 grid((unsigned)a.B * a.nkv * a.qgroups * (a.d / 16));
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), grid, dim3(256), 0, s, a, o); break;
+    case 128: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), grid, dim3(256), 0, s, a, o); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_attn_combine<f16_t, bf16_t>(const AttnArgs&, Frag, hipStream_t);
+template hipError_t launch_attn_combine<float, float>(const AttnArgs&, Frag, hipStream_t);
+
+}  // namespace dflash

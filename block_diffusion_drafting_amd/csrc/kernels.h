@@ -1,0 +1,191 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+//
+// Activation layout.  Every activation matrix X[M][Kd] that feeds a weight
+// product is stored in MFMA fragment order ("frag layout"): m-tile mt,
+// k-block kb, lane l hold 16 bytes = KPL consecutive reduction elements of
+// row mt*16 + l%16 starting at kb*KB + (l/16)*KPL.  A wave loads one
+// fragment with a single coalesced 1 KiB read.  For bf16 models a matrix is
+// a pair of such arrays: `hi` (values rounded to bf16) and `lo` (the
+// rounded remainder); products that use both see about 16 mantissa bits of
+// the activation.  For fp32 models only `hi` (fp32 values) exists.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+#define DFLASH_ROWMAP_MAX 256
+
+namespace dflash {
+
+enum Epi : int {
+  EPI_QKV = 0,     // norm scale, RoPE on q/k, scatter q / block k / block v^T
+  EPI_SWIGLU = 1,  // norm scale, silu(gate) * up -> act (frag layout)
+  EPI_PART = 2,    // write split-K partial tiles (combined by a later kernel)
+  EPI_ARGMAX = 3,  // norm scale, optional logits, per-row argmax keys
+  EPI_FC = 4,      // full context projection rows -> context buffer + staging
+  EPI_KV = 5,      // K (RoPE) / V^T rows -> every layer's cache
+};
+
+// A weight matrix repacked into 16-row x 64-byte blocks (see common.h):
+// tile t (rows 16t..16t+15) holds nkb consecutive 1 KiB blocks.
+struct Packed {
+  const uint8_t* w = nullptr;
+  int32_t n_rows = 0;   // logical rows (before padding to 16)
+  int32_t n_tiles = 0;
+  int32_t kd = 0;       // logical reduction length
+  int32_t nkb = 0;      // 64-byte blocks per row (padded)
+};
+
+// An activation matrix in frag layout.
+struct Frag {
+  u32x4* hi = nullptr;
+  u32x4* lo = nullptr;   // bf16 models only
+  int32_t mtiles = 0;    // allocated m-tiles
+  int32_t nkb = 0;       // k-blocks per m-tile
+};
+
+struct EpiArgs {
+  int32_t M;                // activation rows of the call
+  // RMSNorm scale applied after the product:
+  //   r[m] = rsqrt(sum_g ssq[g*M + m] / norm_dim + eps)
+  const float* ssq;
+  int32_t ssq_groups;
+  int32_t norm_dim;
+  float eps;
+  // geometry
+  int32_t Kblk, Kpad, nq, nkv, d, H, I, V, L;
+  const DevSeq* seqs;
+  const double* inv_freq;   // [d/2] theta^(-2m/d)
+  // outputs
+  void* q;                  // [M][nq*d]          attention type
+  void* bk;                 // [B][nkv][Kpad][d]  attention type
+  void* bvt;                // [B][nkv][d][Kpad]  attention type
+  Frag act;                 // SwiGLU output, frag layout over I
+  float* part;              // split-K partials [nsplit][n_tiles][mtiles][64] f32x4
+  int32_t part_ntiles;
+  int32_t part_mtiles;
+  float* logits;            // [M][V] or null
+  unsigned long long* keys; // [M] argmax keys
+  Frag cbuf;                // context features, frag layout over hidden
+  const RowMap* rowmap;     // [M]
+};
+
+struct GemmArgs {
+  Packed W;
+  // activations: frag layout, or row-major model type (context projection)
+  Frag X;
+  const void* Xrow;
+  int32_t ldx;
+  int32_t M;
+  int32_t kbu;            // k-blocks per unit (split)
+  int32_t nsplit;
+  int32_t n_groups;       // groups of NTG tiles
+  int32_t m_groups;       // groups of MTT m-tiles
+};
+
+struct GemmPlan {
+  int mtt;     // m-tiles per group (1, 2, 4, 8)
+  int ntg;     // tiles per group
+  int kbu, nsplit, n_groups, m_groups;
+  bool split;  // use hi + lo fragments
+  bool rowmajor;
+  size_t part_floats;
+};
+
+GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor);
+
+template <typename T>
+hipError_t launch_gemm(int epi, const GemmPlan& p, const GemmArgs& g, const EpiArgs& e,
+                       hipStream_t s);
+
+struct AttnArgs {
+  const void* q;
+  const void* bk;
+  const void* bvt;
+  const DevSeq* seqs;
+  float* part;            // [B][nkv][qgroups][max_splits][4 waves][d*16 + 32]
+  int32_t B, K, Kpad, nq, nkv, d, layer;
+  int32_t qgroups, chunk, max_splits;
+  float scale_log2;
+};
+size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d);
+template <typename T>
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Merge attention splits in index order; write o (frag layout over nq*d).
+template <typename CT, typename T>
+hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s);
+
+// x[m] = E[id], xg = x * gain -> frag, ssq per 64-column group; keys = 0.
+template <typename T>
+hipError_t launch_embed(const int32_t* ids, const void* embed, const float* gain, int M, int H,
+                        int V, float* x, Frag xg, float* ssq, unsigned long long* keys,
+                        hipStream_t s);
+// x += sum of split-K partials (fixed order); xg = x * gain -> frag; ssq.
+template <typename T>
+hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
+                             const float* gain, Frag xg, float* ssq, hipStream_t s);
+// c = sum of split-K partials -> context buffer rows + staging frag.
+template <typename T>
+hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H,
+                              const RowMap* rowmap, const DevSeq* seqs, Frag cbuf, hipStream_t s);
+// draft ids from argmax keys; optional final-normed hidden rows.
+template <typename T>
+hipError_t launch_finalize(const unsigned long long* keys, int M, int32_t* draft, const float* x,
+                           const float* ssq, int groups, const float* gain, int H, float eps,
+                           void* hidden, hipStream_t s);
+hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int K,
+                         int32_t* out, hipStream_t s);
+template <typename T>
+hipError_t launch_pack(const uint64_t* row_src, int n_rows_padded, int kd, int nkb, uint8_t* dst,
+                       hipStream_t s);
+template <typename T>
+hipError_t launch_to_f32(const void* src, float* dst, int n, hipStream_t s);
+hipError_t launch_rowmap(const int32_t* row_start, int B, int total, const int32_t* positions,
+                         DevSeq* seqs, RowMap* out, hipStream_t s);
+hipError_t launch_set_seq(DevSeq* seqs, int b, DevSeq v, hipStream_t s);
+template <typename T>
+hipError_t launch_grow_copy(DevSeq oldv, DevSeq newv, int L, int nkv, int d, int H,
+                            hipStream_t s);
+hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t s);
+
+// Frag-layout slot (16-byte unit index) of element (m, k) and its position
+// `e` inside the fragment.
+template <typename T>
+__device__ __forceinline__ size_t frag_slot(const Frag& f, int m, int k, int& e) {
+  const int kb = k / Elem<T>::KB;
+  const int r = k - kb * Elem<T>::KB;
+  const int lane = (r / Elem<T>::KPL) * 16 + (m & 15);
+  e = r % Elem<T>::KPL;
+  return ((size_t)(m >> 4) * f.nkb + kb) * WAVE + lane;
+}
+
+// Store N consecutive fp32 values of row m from column k (k % N == 0, N
+// divides KPL) into a frag matrix: hi = round(v), lo = round(v - hi).
+template <typename T, int N>
+__device__ __forceinline__ void frag_store(const Frag& f, int m, int k, const float* v) {
+  int e;
+  const size_t slot = frag_slot<T>(f, m, k, e);
+  if constexpr (sizeof(T) == 2) {
+    bf16_t h[N], l[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      h[i] = f2bf(v[i]);
+      l[i] = f2bf(v[i] - bf2f(h[i]));
+    }
+    auto ph = gp((bf16_t*)(f.hi + slot) + e);
+    auto pl = gp((bf16_t*)(f.lo + slot) + e);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      ph[i] = h[i];
+      pl[i] = l[i];
+    }
+  } else {
+    auto ph = gp((float*)(f.hi + slot) + e);
+#pragma unroll
+    for (int i = 0; i < N; ++i) ph[i] = v[i];
+  }
+}
+
+}  // namespace dflash

@@ -1,0 +1,226 @@
+/*
+ * dflash.h -- C ABI of the DFlash draft-block hot path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (block-diffusion speculative decoding, "DFlash"):
+ *   - kongchang.com, "D-Flash: diffusion drafting speeds LLM inference 3.5x",
+ *     sections "System architecture", "Innovation 1: block-diffusion parallel
+ *     drafting" and "Innovation 2: target-feature KV injection";
+ *   - Google Developers Blog (zh translation on aihot.virxact.com), sections
+ *     "Dual cache for attention", "Smart context management" and "Bridging the
+ *     metadata gap in TPU inference".
+ *
+ * A proposer keeps, per sequence, a context buffer of projected target
+ * features, one static (non-paged) K/V cache per draft layer, and the count
+ * of committed positions that fixes the RoPE offset.  Each step:
+ *   dflash_draft_block  -- one non-causal forward of [anchor, masks...] gives
+ *                          K draft tokens;
+ *   dflash_accept       -- greedy longest-prefix acceptance against the
+ *                          target's tokens gives tau in [1, K+1];
+ *   dflash_project_ctx  -- the tau newly committed positions are projected
+ *                          and appended (never the drafts still being
+ *                          verified), advancing the state by tau.
+ *
+ * Conventions for every entry point:
+ *   - All functions have C linkage, never throw, and return dflash_status.
+ *     On a non-OK status dflash_last_error() gives a message (per thread).
+ *   - "dev" pointers are device memory on the current HIP device; "host"
+ *     pointers are host memory.  The caller owns every input and output
+ *     buffer.  Streams are hipStream_t handles passed as void* (NULL = the
+ *     null stream).  Work is stream-ordered; outputs are valid once the
+ *     stream has reached the call.  Host-side state (ctx_len, cap) is updated
+ *     when the call is enqueued.
+ *   - Arguments are checked before anything is enqueued; a rejected call
+ *     (DFLASH_E_ARG / DFLASH_E_SHAPE / DFLASH_E_STATE) leaves all state
+ *     untouched.  DFLASH_E_HIP reports a failed HIP call; after a device
+ *     fault the context is undefined and must be destroyed.
+ *   - A model is immutable after creation and may be shared by contexts; a
+ *     context must be used from one thread at a time.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_ABI_VERSION 1
+#define DFLASH_MAX_BATCH 256
+#define DFLASH_MAX_K 1024
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_ARG = -1,            /* NULL pointer, out-of-range value            */
+  DFLASH_E_SHAPE = -2,          /* shapes that do not fit the model/context    */
+  DFLASH_E_ALLOC = -3,          /* allocator returned NULL                     */
+  DFLASH_E_HIP = -4,            /* a HIP runtime call failed                   */
+  DFLASH_E_STATE = -5,          /* call not valid in the current state         */
+  DFLASH_E_UNIMPLEMENTED = -6
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Drafter shape.  head_dim must be a multiple of 16, n_q_heads a multiple of
+ * n_kv_heads, intermediate a multiple of 8.  rope_theta is the RoPE base
+ * (rotate-half pairs m, m + head_dim/2, angle p * theta^(-2m/head_dim)),
+ * rms_eps the RMSNorm epsilon. */
+typedef struct {
+  int32_t hidden;
+  int32_t n_layers;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  int32_t vocab;
+  int32_t n_feat;
+  double rope_theta;
+  double rms_eps;
+  dflash_dtype dtype;           /* storage and MFMA input type of weights and
+                                   features (the KV caches: see
+                                   dflash_ctx_buffers) */
+} dflash_config;
+
+/* One draft layer; dev pointers, dtype of the config, row-major [out, in]:
+ *   attn_norm, mlp_norm [hidden]; wq [nq*d, hidden]; wk, wv [nkv*d, hidden];
+ *   wo [hidden, nq*d]; w_gate, w_up [intermediate, hidden];
+ *   w_down [hidden, intermediate]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} dflash_layer_weights;
+
+/* embed [vocab, hidden]; lm_head [vocab, hidden] (may equal embed: tied);
+ * fc [hidden, n_feat*hidden]; final_norm [hidden]; layers: HOST array of
+ * n_layers entries.  Only `embed` is borrowed after dflash_model_create
+ * returns (it must outlive the model); everything else is repacked into
+ * model-owned memory. */
+typedef struct {
+  const void *embed, *lm_head, *fc, *final_norm;
+  const dflash_layer_weights *layers;
+} dflash_weights;
+
+/* Device-memory allocator used for every buffer the library owns.  NULL
+ * allocator = hipMalloc / hipFree.  `free` may be called while work that
+ * used the block is still queued on the stream given to the call that frees
+ * it; the allocator must keep stream-ordered reuse safe (a caching allocator
+ * tied to that stream is). */
+typedef struct {
+  void *(*alloc)(size_t bytes, void *user);
+  void (*free)(void *ptr, void *user);
+  void *user;
+} dflash_allocator;
+
+typedef struct dflash_model dflash_model;
+typedef struct dflash_ctx dflash_ctx;
+
+/* Library version string and ABI version. */
+const char *dflash_version(void);
+int32_t dflash_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread. */
+const char *dflash_last_error(void);
+
+/* Validates the config, allocates model memory through `alloc` and repacks
+ * the weights into tiles laid out for gfx950 MFMA (a private copy; rows of
+ * W_q/W_k are reordered to pair RoPE channels, W_gate/W_up are interleaved,
+ * the per-layer W_k/W_v are stacked for context injection).  The repack runs
+ * on `stream` and is complete when the call returns. */
+dflash_status dflash_model_create(const dflash_config *cfg, const dflash_weights *w,
+                                  const dflash_allocator *alloc, void *stream,
+                                  dflash_model **out);
+dflash_status dflash_model_destroy(dflash_model *m);
+
+/* Weight bytes the hot path streams per draft block (packed matrices plus
+ * gains), for roofline accounting. */
+dflash_status dflash_model_bytes(const dflash_model *m, int64_t *layer_bytes,
+                                 int64_t *lm_head_bytes, int64_t *proj_bytes);
+
+/* Creates proposer state for `batch` sequences (1..DFLASH_MAX_BATCH).
+ * init_cap: host [batch] powers of two, the initial context capacity of each
+ * sequence, or NULL for capacity 0 (buffers are then created by the first
+ * dflash_project_ctx).  All sequences start with ctx_len = 0. */
+dflash_status dflash_ctx_create(const dflash_model *m, int32_t batch, const int32_t *init_cap,
+                                const dflash_allocator *alloc, void *stream,
+                                dflash_ctx **out);
+dflash_status dflash_ctx_destroy(dflash_ctx *c);
+
+/* (a1)-(a3): context projection, append and KV injection.
+ * Appends n_new[b] positions to sequence b: c_j = W_fc feats_j is written to
+ * the context buffer at row ctx_len[b] + j, and for every layer l,
+ * K_l = RoPE(W_k^l c_j, pos_j) and V_l = W_v^l c_j to that layer's cache at
+ * the same row (kongchang.com, "System architecture" and "Innovation 2";
+ * Google Developers Blog, "Smart context management").
+ *   feats     dev [sum(n_new), n_feat*hidden], config dtype, row-major,
+ *             sequences concatenated in batch order.
+ *   n_new     host [batch], each >= 0.  The committed count of the last step
+ *             (tau), never the drafted length.
+ *   positions dev [sum(n_new)] int32 RoPE positions, or NULL for
+ *             ctx_len[b] + j.
+ * If ctx_len[b] + n_new[b] exceeds cap[b], the sequence's buffers are
+ * reallocated with cap = the next power of two of the new length, and the
+ * held rows copied, on `stream`.  Afterwards ctx_len[b] += n_new[b].
+ * Rejects ctx_len + n_new > 2^30 (DFLASH_E_SHAPE). */
+dflash_status dflash_project_ctx(dflash_ctx *c, const void *feats, const int32_t *n_new,
+                                 const int32_t *positions, void *stream);
+
+/* (a4)-(a9): one draft block for every sequence.
+ *   block_ids dev [batch, K] int32: row 0 the anchor (last verified token),
+ *             rows 1..K-1 mask tokens.  Ids outside [0, vocab) are clamped.
+ *   K         1..DFLASH_MAX_K.
+ *   draft_ids dev [batch, K] int32 out: argmax of row i's logits (the draft
+ *             for position ctx_len + 1 + i); ties go to the lowest index.
+ *   logits    dev [batch, K, vocab] float32 out, or NULL.
+ *   hidden    dev [batch, K, hidden] out, config dtype, the final-normed
+ *             hidden state fed to the LM head, or NULL.
+ * Row i sits at position ctx_len[b] + i.  Every layer: RMSNorm, Q/K/V with
+ * RoPE, attention of every block row over the sequence's whole context
+ * and the whole block (no causal mask), output projection + residual,
+ * RMSNorm, SwiGLU MLP + residual; then final RMSNorm, LM head, argmax
+ * (kongchang.com, "System architecture", "Innovation 1"; Google Developers
+ * Blog, "Dual cache for attention").  Does not change the state. */
+dflash_status dflash_draft_block(dflash_ctx *c, const int32_t *block_ids, int32_t K,
+                                 int32_t *draft_ids, float *logits, void *hidden,
+                                 void *stream);
+
+/* (a10): greedy acceptance (Google Developers Blog, "Overcoming the
+ * autoregressive bottleneck"; table 2 caption: greedy decoding).
+ *   draft_ids, target_ids dev [batch, K] int32; accept_len dev [batch] int32
+ *   out: 1 + the number of leading positions where the two agree. */
+dflash_status dflash_accept(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch,
+                            int32_t K, int32_t *accept_len, void *stream);
+
+/* Host copies of the state: ctx_len and cap, host [batch] each (either may
+ * be NULL). */
+dflash_status dflash_ctx_query(const dflash_ctx *c, int32_t *ctx_len, int32_t *cap);
+
+/* Device buffers of sequence b (for tests and snapshots):
+ *   ctxbuf  [phys_rows, hidden] float32           projected features
+ *   k_cache [n_layers, n_kv_heads, phys_rows, head_dim]   RoPE applied
+ *   v_cache [n_layers, n_kv_heads, head_dim, phys_rows]   (transposed)
+ * The caches hold fp16 for DFLASH_BF16 models (same bytes as bf16, finer
+ * rounding; stores saturate at +-65504) and float32 for DFLASH_F32 models.
+ * Rows [0, ctx_len) are valid; phys_rows >= cap.  Pointers change when the
+ * buffers grow. */
+dflash_status dflash_ctx_buffers(const dflash_ctx *c, int32_t b, const void **ctxbuf,
+                                 const void **k_cache, const void **v_cache,
+                                 int32_t *phys_rows);
+
+/* Per-kernel timing with HIP events recorded on the call's stream around
+ * every launch of dflash_project_ctx / dflash_draft_block while enabled.
+ * Phases (index: name): 0 embed, 1 qkv, 2 attention, 3 o_proj, 4 gate_up,
+ * 5 down, 6 lm_head, 7 finalize, 8 fc, 9 kv_inject, 10 grow, 11 rowmap,
+ * 12 attn_combine, 13 resid_norm, 14 fc_finalize.
+ * dflash_profile_read waits for the recorded events, adds their durations
+ * (milliseconds) and launch counts per phase into ms[] / count[] (host
+ * arrays of DFLASH_NUM_PHASES entries, overwritten) and clears the record. */
+#define DFLASH_NUM_PHASES 15
+dflash_status dflash_profile_enable(dflash_ctx *c, int32_t enable);
+dflash_status dflash_profile_read(dflash_ctx *c, double *ms, int64_t *count);
+const char *dflash_phase_name(int32_t phase);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (written here, applied per row): bf16 max |gpu - oracle| /
+max |oracle| <= 2e-2, fp32 <= 1e-4, for logits, final hidden states, the
+context buffer and both KV caches; argmax bit-exact wherever the oracle's
+top-1/top-2 logit margin exceeds 0.05; acceptance lengths, context lengths,
+capacities and buffer row indices bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dflash as O
+from tests.gpu_util import Pair, check_argmax, check_rows, say, to_dev, tol
+
+pytestmark = pytest.mark.gpu
+
+# Small bf16 drafter: several tiles per matrix, ragged vocab tail (4003 rows),
+# GQA with 4 query heads per KV head.
+SMALL = synth.Shape(hidden=512, n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                    intermediate=1408, vocab=4003, n_feat=3, rope_theta=1e6, dtype="bf16")
+SMALL32 = SMALL.replace(dtype="f32", head_dim=64, n_q_heads=8, n_kv_heads=4)
+
+
+_WCACHE = {}
+
+
+def _weights(shape, seed):
+    key = (shape, seed)
+    if key not in _WCACHE:
+        _WCACHE.clear()
+        _WCACHE[key] = synth.weights(shape, seed)
+    return _WCACHE[key]
+
+
+def _prefill(p, lens, seed=5):
+    feats = [synth.prefill_features(p.shape, seed, b, n) for b, n in enumerate(lens)]
+    p.project(feats)
+    return feats
+
+
+def _ids(seed, B, K, V, step=0):
+    return np.stack([synth.block_ids(seed, b, step, K, V) for b in range(B)])
+
+
+def test_mfma_fragment_layout_fp32_tiny():
+    """Tiny fp32 drafter (workload 0 shape) with an empty context and K=1:
+    exercises every kernel with one row, one key, one tile."""
+    say("case: tiny fp32, ctx 0, K 1")
+    p = Pair(synth.TINY, 1000, 1, gain_std=0.1)
+    ids = _ids(3, 1, 1, synth.TINY.vocab)
+    p.compare(ids)
+
+
+@pytest.mark.parametrize("ctx,K", [(64, 8), (0, 8), (1, 3), (130, 37), (200, 16)])
+def test_tiny_fp32_single_block(ctx, K):
+    say(f"case: tiny fp32 ctx={ctx} K={K}")
+    p = Pair(synth.TINY, 1000, 1, gain_std=0.1)
+    if ctx:
+        _prefill(p, [ctx])
+    p.check_state()
+    p.compare(_ids(7, 1, K, synth.TINY.vocab))
+
+
+@pytest.mark.parametrize("B,ctx,K", [(1, 200, 16), (1, 63, 37), (3, 0, 16), (2, 300, 5),
+                                     (1, 100, 128), (2, 70, 130), (1, 5, 300)])
+def test_small_bf16_block(B, ctx, K):
+    say(f"case: small bf16 B={B} ctx={ctx} K={K}")
+    p = Pair(SMALL, 11, B, gain_std=0.1)
+    lens = [ctx + 17 * b for b in range(B)]
+    _prefill(p, lens)
+    p.check_state()
+    p.compare(_ids(13, B, K, SMALL.vocab))
+
+
+def test_small_fp32_block_ragged():
+    say("case: small fp32 B=2 ctx ragged K=21")
+    p = Pair(SMALL32, 12, 2, gain_std=0.1)
+    _prefill(p, [77, 150])
+    p.check_state()
+    p.compare(_ids(14, 2, 21, SMALL32.vocab))
+
+
+def test_padding_rows_never_leak():
+    """NaN in every cache row past ctx_len must not reach any output."""
+    say("case: NaN-poisoned padding")
+    p = Pair(SMALL, 21, 2, gain_std=0.1)
+    _prefill(p, [65, 3])
+    p.poison_padding()
+    g, _ = p.compare(_ids(22, 2, 16, SMALL.vocab))
+    assert np.all(np.isfinite(g["logits"]))
+
+
+def test_non_causal_through_abi():
+    """Changing the last block token changes row 0's logits."""
+    say("case: non-causal")
+    p = Pair(SMALL, 31, 1)
+    _prefill(p, [50])
+    ids = _ids(32, 1, 8, SMALL.vocab)
+    a = p.gpu_draft(ids)["logits"][0, 0]
+    ids2 = ids.copy()
+    ids2[0, -1] = (ids2[0, -1] + 1) % SMALL.vocab
+    b = p.gpu_draft(ids2)["logits"][0, 0]
+    assert np.max(np.abs(a - b)) > 1e-3
+
+
+def test_context_permutation_through_abi():
+    """Projecting the context rows in a permuted order together with their
+    positions gives the same draft outputs (same set of keys and values)."""
+    say("case: context permutation")
+    n = 97
+    p1 = Pair(SMALL, 41, 1)
+    f = synth.prefill_features(SMALL, 42, 0, n)
+    p1.project([f])
+    perm = np.random.default_rng(0).permutation(n)
+    p2 = Pair(SMALL, 41, 1, weights=p1.w)
+    p2.project([f[perm]], positions_per_seq=[perm.astype(np.int32)])
+    ids = _ids(43, 1, 16, SMALL.vocab)
+    a = p1.gpu_draft(ids)
+    b = p2.gpu_draft(ids)
+    # same key/value set in another order: equal within the path's tolerance
+    check_rows("permuted logits", b["logits"][0], a["logits"][0].astype(np.float64), tol(SMALL))
+    # and against the oracle with the permuted projection
+    p2.compare(ids)
+
+
+def test_batch_independence_through_abi():
+    say("case: batch independence")
+    pb = Pair(SMALL, 51, 3)
+    lens = [40, 190, 7]
+    feats = [synth.prefill_features(SMALL, 52, b, n) for b, n in enumerate(lens)]
+    pb.project(feats)
+    ids = _ids(53, 3, 16, SMALL.vocab)
+    gb = pb.gpu_draft(ids)
+    for b in range(3):
+        p1 = Pair(SMALL, 51, 1, weights=pb.w)
+        p1.project([feats[b]])
+        g1 = p1.gpu_draft(ids[b:b + 1])
+        check_rows(f"batch row {b}", gb["logits"][b], g1["logits"][0].astype(np.float64), tol(SMALL))
+
+
+def test_incremental_projection_matches_one_shot():
+    say("case: incremental projection")
+    f = synth.prefill_features(SMALL, 61, 0, 40)
+    p1 = Pair(SMALL, 62, 1)
+    p1.project([f])
+    p2 = Pair(SMALL, 62, 1, weights=p1.w)
+    i = 0
+    for c in (1, 3, 11, 2, 23):
+        p2.project([f[i:i + c]])
+        i += c
+    p1.check_state()
+    p2.check_state()
+    ids = _ids(63, 1, 16, SMALL.vocab)
+    a, b = p1.gpu_draft(ids), p2.gpu_draft(ids)
+    check_rows("incremental logits", b["logits"][0], a["logits"][0].astype(np.float64), tol(SMALL))
+
+
+def test_zero_new_rows_and_multi_sequence_append():
+    say("case: n_new zero rows")
+    p = Pair(SMALL, 71, 3)
+    _prefill(p, [10, 0, 33])
+    p.project([synth.step_features(SMALL, 72, 0, 0, 0), synth.step_features(SMALL, 72, 1, 0, 5),
+               synth.step_features(SMALL, 72, 2, 0, 0)])
+    p.check_state()
+    p.compare(_ids(73, 3, 4, SMALL.vocab))
+
+
+def test_accept_kernel_exhaustive_patterns():
+    """Every match pattern at K = 10, plus K spanning several waves."""
+    import block_diffusion_drafting_amd as dfl
+    say("case: accept patterns")
+    K = 10
+    pats = np.array([[(m >> i) & 1 for i in range(K)] for m in range(1 << K)], np.int32)
+    B = len(pats)
+    draft = np.tile(np.arange(K, dtype=np.int32), (B, 1))
+    target = np.where(pats == 1, draft, draft + 7).astype(np.int32)
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    dfl.dflash_accept(to_dev(draft), to_dev(target), B, K, out)
+    assert np.array_equal(out.cpu().numpy(), O.accept(draft, target))
+    for K in (1, 63, 64, 65, 130, 1024):
+        rng = np.random.default_rng(K)
+        B = 50
+        d = rng.integers(0, 5, size=(B, K)).astype(np.int32)
+        t = d.copy()
+        cut = rng.integers(0, K + 1, size=B)
+        for b in range(B):
+            if cut[b] < K:
+                t[b, cut[b]] += 1
+        out = torch.empty(B, dtype=torch.int32, device="cuda")
+        dfl.dflash_accept(to_dev(d), to_dev(t), B, K, out)
+        assert np.array_equal(out.cpu().numpy(), O.accept(d, t))
+
+
+def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=()):
+    """GPU session and oracle session in lockstep; tau, ctx_len and cap must
+    be identical every step; outputs compared on the checked steps."""
+    import block_diffusion_drafting_amd as dfl
+    seqs = list(range(wl.batch)) if batch_seqs is None else batch_seqs
+    w = _weights(shape, wl.seed)
+    p = Pair(shape, wl.seed, wl.batch, weights=w, oracle_seqs=[])
+    feats = [synth.prefill_features(shape, wl.seed, b, wl.ctx0[b]) for b in range(wl.batch)]
+    p.project(feats)                      # GPU only: the oracle session prefills itself
+    osess = O.Session(p.om, wl, keep_outputs=True, seqs=seqs)
+    p.oseqs = list(seqs)
+    p.ost = {b: osess.states[i] for i, b in enumerate(seqs)}
+    anchors = [synth.first_anchor(wl.seed, b, shape.vocab) for b in range(wl.batch)]
+    p.check_state()
+    K = wl.K
+    for t in range(steps):
+        ids = np.stack([synth.block_ids(wl.seed, b, t, K, shape.vocab) for b in range(wl.batch)])
+        ids[:, 0] = anchors
+        check = (t % check_every == 0) or (t in tail_check) or t == steps - 1
+        g = p.gpu_draft(ids, logits=check, hidden=False)
+        draws = [synth.verifier_draws(wl.seed, b, t, K, shape.vocab, wl.a[b], wl.gamma) for b in range(wl.batch)]
+        target = np.stack([synth.target_tokens(g["draft"][b], draws[b], shape.vocab) for b in range(wl.batch)])
+        tau_d = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+        dfl.dflash_accept(to_dev(g["draft"].astype(np.int32)), to_dev(target), wl.batch, K, tau_d)
+        tau = tau_d.cpu().numpy()
+        rec = osess.step(draft=check)
+        assert np.array_equal(rec.block_ids, ids[seqs])
+        assert np.array_equal(tau[seqs], rec.tau), (t, tau[seqs], rec.tau)
+        if check:
+            for i, b in enumerate(seqs):
+                check_rows(f"step {t} logits[{b}]", g["logits"][b], rec.logits[i], tol(shape))
+                check_argmax(g["draft"][b], rec.logits[i])
+        # commit tau positions on the GPU side (oracle did it inside step)
+        fe = [synth.step_features(shape, wl.seed, b, t, int(tau[b])) for b in range(wl.batch)]
+        p.dfl.dflash_project_ctx(p.ctx, to_dev(np.concatenate(fe, axis=0)), [int(x) for x in tau])
+        anchors = [draws[b].bonus for b in range(wl.batch)]
+        lens, caps = p.ctx.query()
+        assert [lens[b] for b in seqs] == rec.ctx_len.tolist()
+        assert [caps[b] for b in seqs] == rec.cap.tolist()
+        assert osess.violations() == []
+        say(f"  step {t}: tau={tau.tolist()[:4]} ctx={lens[:4]} cap={caps[:4]}")
+    p.check_state()
+    return p
+
+
+def test_session_workload0_tiny_fp32():
+    """The tiny fp32 workload: 8 steps, every step compared."""
+    say("case: session workload 0")
+    wl = synth.workload(0)
+    _session(wl.shape, wl, wl.steps)
+
+
+def test_session_small_bf16_growth():
+    say("case: session small bf16 with growth")
+    wl = synth.workload(2).replace(shape=SMALL, ctx0=(60, 5), batch=2, a=(0.9, 0.7), K=10)
+    _session(SMALL, wl, 12)
+
+
+@pytest.mark.slow
+def test_workload1_qwen3_4b_shape_full_size():
+    """Qwen3-4B-shaped drafter at full size: prefill 2048, one block compared
+    in full, then a 16-step session (tau/ctx/cap every step, logits at
+    steps 0, 7, 15)."""
+    say("case: workload 1 full size")
+    wl = synth.workload(1)
+    _session(wl.shape, wl, wl.steps, check_every=8)
+
+
+@pytest.mark.slow
+def test_workload2_llama_shape_growth_session():
+    """Llama-3.1-8B-shaped drafter, 64 steps of K=10 appends from a full
+    4096-row buffer (grows to 8192 on the first step); outputs compared at
+    steps 0, 1, 32, 63; tau/ctx/cap every step."""
+    say("case: workload 2 full size")
+    wl = synth.workload(2)
+    _session(wl.shape, wl, wl.steps, check_every=32, tail_check=(1,))
+
+
+@pytest.mark.slow
+def test_workload4_batched_long_context_sampled():
+    """Batch 16, contexts 1k-32k: the GPU runs all 16 sequences; the oracle
+    follows two sampled sequences (the shortest and one mid-length) for the
+    whole session, compared at steps 0, 1 and the last."""
+    say("case: workload 4 sampled")
+    wl = synth.workload(4).replace(steps=32)
+    order = np.argsort(wl.ctx0)
+    seqs = sorted({int(order[0]), int(order[5])})
+    _session(wl.shape, wl, wl.steps, check_every=31, batch_seqs=seqs, tail_check=(1,))
+
+
+_K_SWEEP = {}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("K", [16, 32, 64, 128, 1024])
+def test_workload3_k_sweep_blocks(K):
+    """Qwen3-4B shape, context 4096, each block size of the sweep (one
+    prefilled context shared by the five block sizes)."""
+    say(f"case: workload 3 K={K}")
+    wl = synth.workload(3)
+    if "p" not in _K_SWEEP:
+        p = Pair(wl.shape, wl.seed, 1, weights=_weights(wl.shape, wl.seed))
+        _prefill(p, [4096], seed=wl.seed)
+        p.check_state()
+        _K_SWEEP["p"] = p
+    p = _K_SWEEP["p"]
+    ids = _ids(wl.seed, 1, K, wl.shape.vocab)
+    _, stats = p.compare(ids, hidden=(K <= 128))
+    say(f"  errors {stats}")
