@@ -94,7 +94,7 @@ def _load() -> ctypes.CDLL:
         "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
         "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                 ctypes.POINTER(vp), i32p], ctypes.c_int),
-        "dflash_profile_enable": ([vp, i32], ctypes.c_int),
+        "dflash_profile_enable": ([vp, ctypes.c_uint32], ctypes.c_int),
         "dflash_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), i64p], ctypes.c_int),
         "dflash_phase_name": ([i32], ctypes.c_char_p),
     }
@@ -255,8 +255,22 @@ class Context:
                                                             ctypes.byref(phys)))
         return c.value, k.value, v.value, phys.value
 
-    def profile(self, enable: bool) -> None:
-        _check("dflash_profile_enable", lib.dflash_profile_enable(self.handle, 1 if enable else 0))
+    def profile(self, enable=True) -> None:
+        """Time phases with HIP events: True = every phase, False = off, a
+        name or a list of names = those phases only."""
+        if enable is True:
+            mask = (1 << NUM_PHASES) - 1
+        elif not enable:
+            mask = 0
+        else:
+            names = [enable] if isinstance(enable, str) else list(enable)
+            known = [lib.dflash_phase_name(i).decode() for i in range(NUM_PHASES)]
+            mask = 0
+            for n in names:
+                if n not in known:
+                    raise ValueError(f"unknown phase {n!r}")
+                mask |= 1 << known.index(n)
+        _check("dflash_profile_enable", lib.dflash_profile_enable(self.handle, mask))
 
     def profile_read(self):
         """{phase name: (total ms, launches)} since the last read."""

@@ -9,15 +9,17 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "misc.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm_qkv.hip", "gemm_swiglu.hip", "gemm_part.hip", "gemm_argmax.hip",
+           "gemm_proj.hip", "attention.hip", "misc.hip"]
 LIB = os.path.join(HERE, "libdflash.so")
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -27,17 +29,33 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *srcs, "-o", tmp]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if NOISE not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel) and links the
+    shared library; objects go to a build folder beside the sources."""
+    from concurrent.futures import ThreadPoolExecutor
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        jobs.append((obj, [cc, *HIPCC_FLAGS, "-c", os.path.join(HERE, "csrc", src), "-o", obj]))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        errs = list(ex.map(lambda j: _run(j[1]), jobs))
+    tmp = LIB + ".tmp"
+    errs.append(_run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e, file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -95,7 +95,7 @@ static const char* kPhaseNames[DFLASH_NUM_PHASES] = {
     "grow", "rowmap", "attn_combine", "resid_norm", "fc_finalize"};
 
 struct Profiler {
-  bool on = false;
+  uint32_t mask = 0;   // bit p: time phase p
   std::vector<hipEvent_t> pool;
   size_t used = 0;
   std::vector<std::pair<int, size_t>> recs;  // (phase, index of start event)
@@ -161,19 +161,19 @@ dflash_status ensure_frag(dflash_ctx* c, Buf& hi, Buf& lo, bool pair, int mtiles
 // Records a start event now and the end event when destroyed (profiling on).
 struct PhaseTimer {
   dflash_ctx* c;
-  int phase;
   hipStream_t s;
-  bool active = false;
-  PhaseTimer(dflash_ctx* c_, int ph, hipStream_t s_) : c(c_), phase(ph), s(s_) {
-    if (!c->prof.on) return;
+  hipEvent_t end = nullptr;
+  PhaseTimer(dflash_ctx* c_, int ph, hipStream_t s_) : c(c_), s(s_) {
+    if (!(c->prof.mask >> ph & 1u)) return;
     hipEvent_t a = c->prof.get();
     hipEvent_t b = c->prof.get();
     if (!a || !b) return;
-    c->prof.recs.push_back({phase, c->prof.used - 2});
-    active = hipEventRecord(a, s) == hipSuccess;
+    if (hipEventRecord(a, s) != hipSuccess) return;
+    c->prof.recs.push_back({ph, c->prof.used - 2});
+    end = b;
   }
   ~PhaseTimer() {
-    if (active) (void)hipEventRecord(c->prof.pool[c->prof.recs.back().second + 1], s);
+    if (end) (void)hipEventRecord(end, s);
   }
 };
 
@@ -638,10 +638,11 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
     work += (int64_t)(c->seq[b].ctx_len + K) * nkv * qgroups;
     max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
   }
-  // keys per split: a multiple of 64, at least 256 (several chunks per
-  // workgroup), larger when there is enough work for ~512 workgroups
+  // keys per split: a multiple of 64 giving about 512 workgroups, and at
+  // least 128 (at short contexts the split count, not the chunk size, sets
+  // the cost of the combine)
   int chunk = 64 * (int)((work + 64 * 512 - 1) / (64 * 512));
-  if (chunk < 256) chunk = 256;
+  if (chunk < 128) chunk = 128;
   const int max_splits = (max_len + chunk - 1) / chunk + (K + chunk - 1) / chunk;
   if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d) * sizeof(float))))
     return st;
@@ -730,9 +731,9 @@ dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* block_ids, int32_
                                         : draft_impl<float>(c, block_ids, K, draft_ids, logits, hidden, s);
 }
 
-dflash_status dflash_profile_enable(dflash_ctx* c, int32_t enable) {
+dflash_status dflash_profile_enable(dflash_ctx* c, uint32_t phase_mask) {
   if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
-  c->prof.on = enable != 0;
+  c->prof.mask = phase_mask & ((1u << DFLASH_NUM_PHASES) - 1u);
   return DFLASH_OK;
 }
 

@@ -252,14 +252,19 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   }
 }
 
-// One workgroup per (sequence, KV head, query group, 16-row d-tile); wave w
-// merges query tile 4*qg + w over the splits in index order and writes its
-// part of o (frag layout of the model type T over nq*d, input of the output
-// projection).
+// One workgroup per (sequence, KV head, query group, 16-row d-tile), 16
+// waves: wave w handles query tile 4*qg + w%4 over the quarter w/4 of the
+// splits (its loads all issued at once), then the quarters are merged in
+// order through LDS.  Writes its part of o (frag layout of the model type T
+// over nq*d, input of the output projection).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, Frag out) {
+__global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out) {
   constexpr int NDT = D / 16;
+  constexpr int BATCH = 8;
+  __shared__ float sm[4][4][64], sl[4][4][64];
+  __shared__ f32x4 so[4][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qt = wave & 3, quarter = wave >> 2;
   const int g4 = lane >> 4, col = lane & 15;
   int u = blockIdx.x;
   const int t = u % NDT;
@@ -270,27 +275,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, Frag out)
   const int b = u / a.nkv;
   const int ctx_len = a.seqs[b].ctx_len;
   const int n_s = (ctx_len + a.chunk - 1) / a.chunk + (a.K + a.chunk - 1) / a.chunk;
-  const int rep = a.nq / a.nkv;
-  const int r = (qg * 4 + wave) * 16 + col;
-  if (r >= a.K * rep) return;
-  const int h = g * rep + r / a.K, i = r % a.K;
+  const int per = (n_s + 3) / 4;
+  const int s_begin = min(n_s, quarter * per), s_end = min(n_s, s_begin + per);
   const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
   const size_t wstride = (size_t)D * 16 + 32;
-  const float* base = a.part + (unit * a.max_splits * 4 + wave) * wstride;
-  const size_t sstride = 4 * wstride;   // next split, same wave
-  // online merge in split order; loads are issued eight splits at a time
+  const float* base = a.part + (unit * a.max_splits * 4 + qt) * wstride;
+  const size_t sstride = 4 * wstride;   // next split, same query tile
   float M = -INFINITY, L = 0.f;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n_s; s0 += 8) {
-    float ms[8], ls[8];
-    f32x4 os[8];
+  for (int s0 = s_begin; s0 < s_end; s0 += BATCH) {
+    float ms[BATCH], ls[BATCH];
+    f32x4 os[BATCH];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (s0 + k < n_s) {
+    for (int k = 0; k < BATCH; ++k) {
+      if (s0 + k < s_end) {
         const float* pp = base + (s0 + k) * sstride;
-        ms[k] = pp[D * 16 + col];
-        ls[k] = pp[D * 16 + 16 + col];
-        os[k] = *(const f32x4*)(pp + (t * 64 + lane) * 4);
+        ms[k] = gld(pp + D * 16 + col);
+        ls[k] = gld(pp + D * 16 + 16 + col);
+        os[k] = gld((const f32x4*)(pp + (t * 64 + lane) * 4));
       } else {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, Frag out)
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < BATCH; ++k) {
       if (ms[k] == -INFINITY) continue;
       const float Mn = fmaxf(M, ms[k]);
       const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
@@ -308,6 +310,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, Frag out)
       M = Mn;
     }
   }
+  sm[quarter][qt][lane] = M;
+  sl[quarter][qt][lane] = L;
+  so[quarter][qt][lane] = o;
+  __syncthreads();
+  if (quarter != 0) return;
+  M = -INFINITY;
+  L = 0.f;
+  o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float mk = sm[k][qt][lane];
+    if (mk == -INFINITY) continue;
+    const float Mn = fmaxf(M, mk);
+    const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+    const float a1 = exp2f(mk - Mn);
+    L = L * a0 + sl[k][qt][lane] * a1;
+    o = o * a0 + so[k][qt][lane] * a1;
+    M = Mn;
+  }
+  const int rep = a.nq / a.nkv;
+  const int r = (qg * 4 + qt) * 16 + col;
+  if (r >= a.K * rep) return;
+  const int h = g * rep + r / a.K, i = r % a.K;
   const float inv = 1.f / L;
   float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   frag_store<T, 4>(out, b * a.K + i, h * D + t * 16 + g4 * 4, v);
@@ -331,8 +356,8 @@ template <typename CT, typename T>
 hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s) {
   dim3 grid((unsigned)a.B * a.nkv * a.qgroups * (a.d / 16));
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), grid, dim3(256), 0, s, a, o); break;
-    case 128: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), grid, dim3(256), 0, s, a, o); break;
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), grid, dim3(1024), 0, s, a, o); break;
+    case 128: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), grid, dim3(1024), 0, s, a, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

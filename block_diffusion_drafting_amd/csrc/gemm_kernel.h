@@ -1,0 +1,412 @@
+// Weight-streaming products of the draft block (kernel and launch templates), Y^T = W X^T, with W
+// repacked into MFMA fragments and the fused epilogue of each projection.
+//
+// At K*batch <= 128 activation rows every weight byte feeds at most 128
+// multiply-adds, so these products are bound by streaming W from HBM.  The
+// kernel is built so that a launch is one uninterrupted stream:
+//   * a workgroup owns NTG 16-row tiles of W and a range of k-blocks; its
+//     four waves split that range, each loading CHK weight fragments per
+//     tile (1 KiB coalesced reads) and the matching activation fragments
+//     (frag layout, from L2), then issuing the MFMAs;
+//   * the four partial sums are added through LDS in wave order and the
+//     epilogue runs on complete sums inside the workgroup;
+//   * nothing in a launch waits for another workgroup: products split over
+//     k across workgroups (EPI_PART) write their partial tiles with plain
+//     stores, and the next kernel adds them in split order.  Results are
+//     therefore deterministic, and no device-scope fence (an L2 writeback +
+//     invalidate on this GPU) is ever executed.
+// Rows of the activation matrix beyond M are computed but never stored.
+#pragma once
+
+#include "kernels.h"
+
+namespace dflash {
+
+// ---------------------------------------------------------------------------
+// epilogue helpers
+// ---------------------------------------------------------------------------
+// RMSNorm scale of row m from the per-column-group sums of squares; the
+// loads are independent so they are issued together.
+__device__ __forceinline__ float norm_scale(const EpiArgs& e, int m) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int g = 0;
+  for (; g + 8 <= e.ssq_groups; g += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += e.ssq[(size_t)(g + i) * e.M + m];
+  }
+  for (; g < e.ssq_groups; ++g) acc[0] += e.ssq[(size_t)g * e.M + m];
+  const float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  return rsqrtf(s / (float)e.norm_dim + e.eps);
+}
+
+constexpr bool needs_norm(int epi) { return epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_ARGMAX; }
+
+__device__ __forceinline__ void rope_pair(float x1, float x2, int pos, double inv, float& o1,
+                                          float& o2) {
+  double sn, cs;
+  sincos((double)pos * inv, &sn, &cs);
+  const float c = (float)cs, s = (float)sn;
+  o1 = x1 * c - x2 * s;
+  o2 = x2 * c + x1 * s;
+}
+
+__device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m);
+  hi = __shfl_xor(hi, m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// One complete 16x16 output tile: acc[j] is output row n = tile*16 +
+// 4*(lane/16) + j of activation row m = mt*16 + lane%16.  Runs on one wave.
+template <typename T, int EPI>
+__device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 acc, int lane,
+                              float r, unsigned long long* kmax) {
+  using CT = typename CacheOf<T>::type;
+  const int g4 = lane >> 4;
+  const int m = mt * 16 + (lane & 15);
+  if constexpr (EPI == EPI_PART) {
+    if (mt >= e.part_mtiles) return;   // m-tile past the rows of the call: no slot
+    *gp((f32x4*)(e.part + ((((size_t)s * e.part_ntiles + tile) * e.part_mtiles + mt) * 64 + lane) * 4)) = acc;
+    return;
+  }
+  if (m >= e.M) return;
+  if constexpr (EPI == EPI_QKV) {
+    const int qd = e.nq * e.d, kvd = e.nkv * e.d;
+    const int n = tile * 16;
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = acc[j] * r;
+    const int b = m / e.Kblk, i = m - b * e.Kblk;
+    const int pos = e.seqs[b].ctx_len + i;
+    if (n < qd + kvd) {
+      const bool isq = n < qd;
+      const int nn = isq ? n : n - qd;
+      const int head = nn / e.d, th = (nn % e.d) / 16;
+      const int p0 = th * 8 + g4 * 2;
+      float a1, a2, b1, b2;
+      rope_pair(y[0], y[1], pos, e.inv_freq[p0], a1, a2);
+      rope_pair(y[2], y[3], pos, e.inv_freq[p0 + 1], b1, b2);
+      auto dst = gp(isq ? (CT*)e.q + (size_t)m * qd + head * e.d
+                        : (CT*)e.bk + (((size_t)b * e.nkv + head) * e.Kpad + i) * e.d);
+      const int h2 = e.d / 2;
+      dst[p0] = Elem<CT>::from_f(a1);
+      dst[p0 + 1] = Elem<CT>::from_f(b1);
+      dst[p0 + h2] = Elem<CT>::from_f(a2);
+      dst[p0 + 1 + h2] = Elem<CT>::from_f(b2);
+    } else {
+      const int nn = n - qd - kvd;
+      const int head = nn / e.d, f0 = nn % e.d + g4 * 4;
+      auto dst = gp((CT*)e.bvt + (((size_t)b * e.nkv + head) * e.d + f0) * e.Kpad + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[(size_t)j * e.Kpad] = Elem<CT>::from_f(y[j]);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // tile rows 4*g4 + j: gate f, up f, gate f+1, up f+1 with f = tile*8 + 2*g4
+    float v[2] = {silu(acc[0] * r) * (acc[1] * r), silu(acc[2] * r) * (acc[3] * r)};
+    frag_store<T, 2>(e.act, m, tile * 8 + g4 * 2, v);
+  } else if constexpr (EPI == EPI_ARGMAX) {
+    const int n = tile * 16 + g4 * 4;
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = acc[j] * r;
+    if (e.logits) {
+      auto lp = gp(e.logits + (size_t)m * e.V + n);
+      if (n + 4 <= e.V && (e.V & 3) == 0) {
+        *gp((f32x4*)(e.logits + (size_t)m * e.V + n)) = f32x4{y[0], y[1], y[2], y[3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n + j < e.V) lp[j] = y[j];
+      }
+    }
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (n + j < e.V) {
+        const unsigned long long k = argmax_key(y[j], (uint32_t)(n + j));
+        best = k > best ? k : best;
+      }
+    }
+    atomicMax(kmax + (lane & 15), best);   // LDS, per column of this m-tile
+  } else if constexpr (EPI == EPI_FC) {
+    const int n = tile * 16 + g4 * 4;
+    const RowMap rm = e.rowmap[m];
+    *gp((f32x4*)((float*)e.seqs[rm.b].ctxbuf + (size_t)rm.slot * e.H + n)) = acc;
+    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+    frag_store<T, 4>(e.cbuf, m, n, v);
+  } else if constexpr (EPI == EPI_KV) {
+    const int kvd = e.nkv * e.d;
+    const int n = tile * 16;
+    const int l = n / (2 * kvd);
+    const int nn = n - l * 2 * kvd;
+    const RowMap rm = e.rowmap[m];
+    const DevSeq sq = e.seqs[rm.b];
+    if (nn < kvd) {
+      const int head = nn / e.d, th = (nn % e.d) / 16;
+      const int p0 = th * 8 + g4 * 2;
+      float a1, a2, b1, b2;
+      rope_pair(acc[0], acc[1], rm.pos, e.inv_freq[p0], a1, a2);
+      rope_pair(acc[2], acc[3], rm.pos, e.inv_freq[p0 + 1], b1, b2);
+      auto dst = gp((CT*)sq.k + (((size_t)l * e.nkv + head) * sq.phys + rm.slot) * e.d);
+      const int h2 = e.d / 2;
+      dst[p0] = Elem<CT>::from_f(a1);
+      dst[p0 + 1] = Elem<CT>::from_f(b1);
+      dst[p0 + h2] = Elem<CT>::from_f(a2);
+      dst[p0 + 1 + h2] = Elem<CT>::from_f(b2);
+    } else {
+      const int v = nn - kvd;
+      const int head = v / e.d, f0 = v % e.d + g4 * 4;
+      auto dst = gp((CT*)sq.vt + (((size_t)l * e.nkv + head) * e.d + f0) * sq.phys + rm.slot);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[(size_t)j * sq.phys] = Elem<CT>::from_f(acc[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the product kernel
+// ---------------------------------------------------------------------------
+// Activation fragment(s) of m-tile mt, k-block kb (zero outside the matrix).
+template <typename T, bool ROW, bool SPLIT>
+__device__ __forceinline__ void load_x(const GemmArgs& g, int mt, int kb, int lane, u32x4& hi,
+                                       u32x4& lo) {
+  using E = Elem<T>;
+  hi = u32x4{0u, 0u, 0u, 0u};
+  lo = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (ROW) {
+    const int row = mt * 16 + (lane & 15);
+    const int k = kb * E::KB + (lane >> 4) * E::KPL;
+    if (row < g.M && k < g.W.kd) hi = *(const u32x4*)((const T*)g.Xrow + (size_t)row * g.ldx + k);
+  } else {
+    if (mt < g.X.mtiles) {
+      const size_t slot = ((size_t)mt * g.X.nkb + kb) * WAVE + lane;
+      hi = g.X.hi[slot];
+      if constexpr (SPLIT) lo = g.X.lo[slot];
+    }
+  }
+}
+
+// Default k-blocks per load batch: up to 16 weight and 16 activation
+// fragments per wave in flight.
+template <int MTT, int NTG, bool SPLIT>
+struct DefaultChk {
+  static constexpr int XF = MTT * (SPLIT ? 2 : 1);
+  static constexpr int C0 = (16 / NTG) < (16 / XF) ? (16 / NTG) : (16 / XF);
+  static constexpr int value = C0 < 1 ? 1 : C0;
+};
+
+template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT, int WAVES = 4,
+          int CHK = DefaultChk<MTT, NTG, SPLIT>::value>
+__global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e) {
+  using E = Elem<T>;
+  constexpr int ITEMS = NTG * MTT;
+  __shared__ f32x4 red[WAVES][ITEMS][WAVE];
+  __shared__ unsigned long long kmax[MTT][16];
+  __shared__ float rnorm[MTT * 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int u = blockIdx.x;
+  const int s = u % g.nsplit;
+  u /= g.nsplit;
+  const int ng = u % g.n_groups;
+  const int mg = u / g.n_groups;
+  // balanced tile ranges: group ng owns tiles [tile0, tile0 + nt), nt <= NTG
+  const int tile0 = (int)((long)ng * g.W.n_tiles / g.n_groups);
+  const int nt = (int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0;
+  const int mt0 = mg * MTT;
+  const int kbA = s * g.kbu;
+  const int kbB = min(g.W.nkb, kbA + g.kbu);
+  const int per = (kbB - kbA + WAVES - 1) / WAVES;
+  const int kw0 = kbA + wave * per;
+  const int kw1 = min(kbB, kw0 + per);
+
+  const uint8_t* wb[NTG];
+#pragma unroll
+  for (int t = 0; t < NTG; ++t) {
+    const int tile = min(tile0 + t, g.W.n_tiles - 1);   // out-of-range tiles: read a valid one, never stored
+    wb[t] = g.W.w + (size_t)tile * g.W.nkb * BLOCK_BYTES + lane * FRAG_BYTES;
+  }
+  f32x4 acc[NTG][MTT];
+#pragma unroll
+  for (int t = 0; t < NTG; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the norm scale of this workgroup's rows, loaded while the weights stream
+  if constexpr (needs_norm(EPI)) {
+    if (threadIdx.x < MTT * 16) {
+      const int m = mt0 * 16 + threadIdx.x;
+      rnorm[threadIdx.x] = m < e.M ? norm_scale(e, m) : 0.f;
+    }
+  }
+
+  for (int kb = kw0; kb < kw1; kb += CHK) {
+    u32x4 wf[NTG][CHK];
+    u32x4 xh[MTT][CHK], xl[MTT][CHK];
+#pragma unroll
+    for (int j = 0; j < CHK; ++j) {
+      const bool ok = kb + j < kw1;
+#pragma unroll
+      for (int t = 0; t < NTG; ++t)
+        wf[t][j] = (ok && t < nt)
+                       ? __builtin_nontemporal_load((const u32x4*)(wb[t] + (size_t)(kb + j) * BLOCK_BYTES))
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < CHK; ++j) {
+      const bool ok = kb + j < kw1;
+#pragma unroll
+      for (int mt = 0; mt < MTT; ++mt) {
+        if (ok)
+          load_x<T, ROW, SPLIT>(g, mt0 + mt, kb + j, lane, xh[mt][j], xl[mt][j]);
+        else
+          xh[mt][j] = xl[mt][j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CHK; ++j)
+#pragma unroll
+      for (int t = 0; t < NTG; ++t) {
+        if (t >= nt) continue;   // uniform over the workgroup
+#pragma unroll
+        for (int mt = 0; mt < MTT; ++mt) {
+          acc[t][mt] = E::mma(wf[t][j], xh[mt][j], acc[t][mt]);
+          if constexpr (SPLIT) acc[t][mt] = E::mma(wf[t][j], xl[mt][j], acc[t][mt]);
+        }
+      }
+  }
+
+  // add the waves' sums in wave order
+#pragma unroll
+  for (int t = 0; t < NTG; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt) red[wave][t * MTT + mt][lane] = acc[t][mt];
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (threadIdx.x < MTT * 16) (&kmax[0][0])[threadIdx.x] = 0ull;
+  }
+  __syncthreads();
+  for (int it = wave; it < nt * MTT; it += WAVES) {
+    const int t = it / MTT, mt = it % MTT;
+    const int tile = tile0 + t;
+    f32x4 sum = red[0][it][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][it][lane];
+    epilogue_tile<T, EPI>(e, s, tile, mt0 + mt, sum, lane, rnorm[mt * 16 + (lane & 15)], kmax[mt]);
+  }
+  if constexpr (EPI == EPI_ARGMAX) {
+    __syncthreads();
+    if (threadIdx.x < MTT * 16) {
+      const int m = (mt0 + threadIdx.x / 16) * 16 + (threadIdx.x & 15);
+      const unsigned long long k = (&kmax[0][0])[threadIdx.x];
+      if (m < e.M && k) atomicMax(e.keys + m, k);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch of one compiled variant (instantiated per epilogue in gemm_<epi>.hip)
+// ---------------------------------------------------------------------------
+// k-blocks per load batch: about 20 weight fragments per wave in flight for
+// one m-tile, fewer activation fragments for more m-tiles
+template <int MTT, int NTG, bool SPLIT>
+struct HotChk {
+  static constexpr int W = NTG <= 2 ? 10 : 20 / NTG;       // weight-fragment bound
+  static constexpr int X = 16 / (MTT * (SPLIT ? 2 : 1));   // activation-fragment bound
+  static constexpr int C = MTT == 1 ? W : (W < X ? W : X);
+  static constexpr int value = C < 1 ? 1 : C;
+};
+
+template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT, int WAVES, int CHK>
+inline hipError_t launch_v(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  dim3 grid((unsigned)p.n_groups * p.m_groups * p.nsplit);
+  hipLaunchKernelGGL((gemm_kernel<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK>), grid, dim3(WAVES * 64), 0, s, g,
+                     e);
+  return hipGetLastError();
+}
+
+template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT>
+inline hipError_t launch_h(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  constexpr int WAVES = MTT == 1 ? 8 : 4;
+  return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, HotChk<MTT, NTG, SPLIT>::value>(p, g, e, s);
+}
+
+template <typename T, int EPI, bool ROW, bool SPLIT>
+inline hipError_t launch_hot(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  switch (p.mtt) {
+    case 1:
+      switch (p.ntg) {
+        case 1: return launch_h<T, 1, 1, EPI, ROW, SPLIT>(p, g, e, s);
+        case 2: return launch_h<T, 1, 2, EPI, ROW, SPLIT>(p, g, e, s);
+        case 4: return launch_h<T, 1, 4, EPI, ROW, SPLIT>(p, g, e, s);
+        case 5: return launch_h<T, 1, 5, EPI, ROW, SPLIT>(p, g, e, s);
+        case 6: return launch_h<T, 1, 6, EPI, ROW, SPLIT>(p, g, e, s);
+        case 8: return launch_h<T, 1, 8, EPI, ROW, SPLIT>(p, g, e, s);
+      }
+      break;
+    case 2:
+      switch (p.ntg) {
+        case 1: return launch_h<T, 2, 1, EPI, ROW, SPLIT>(p, g, e, s);
+        case 2: return launch_h<T, 2, 2, EPI, ROW, SPLIT>(p, g, e, s);
+        case 4: return launch_h<T, 2, 4, EPI, ROW, SPLIT>(p, g, e, s);
+        case 8: return launch_h<T, 2, 8, EPI, ROW, SPLIT>(p, g, e, s);
+      }
+      break;
+    case 4:
+      switch (p.ntg) {
+        case 1: return launch_h<T, 4, 1, EPI, ROW, SPLIT>(p, g, e, s);
+        case 2: return launch_h<T, 4, 2, EPI, ROW, SPLIT>(p, g, e, s);
+        case 4: return launch_h<T, 4, 4, EPI, ROW, SPLIT>(p, g, e, s);
+      }
+      break;
+    default:
+      switch (p.ntg) {
+        case 1: return launch_h<T, 8, 1, EPI, ROW, SPLIT>(p, g, e, s);
+        case 2: return launch_h<T, 8, 2, EPI, ROW, SPLIT>(p, g, e, s);
+      }
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int EPI, bool ROW, bool SPLIT>
+inline hipError_t launch_fixed(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  constexpr int NTG = EPI == EPI_FC ? 4 : 2;
+  if (p.ntg != NTG) return hipErrorInvalidValue;
+  switch (p.mtt) {
+    case 1: return launch_v<T, 1, NTG, EPI, ROW, SPLIT, 4, 4>(p, g, e, s);
+    case 2: return launch_v<T, 2, NTG, EPI, ROW, SPLIT, 4, DefaultChk<2, NTG, SPLIT>::value>(p, g, e, s);
+    case 4: return launch_v<T, 4, NTG, EPI, ROW, SPLIT, 4, DefaultChk<4, NTG, SPLIT>::value>(p, g, e, s);
+    default: return launch_v<T, 8, NTG, EPI, ROW, SPLIT, 4, DefaultChk<8, NTG, SPLIT>::value>(p, g, e, s);
+  }
+}
+
+template <typename T, int EPI>
+hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  g.kbu = p.kbu;
+  g.nsplit = p.nsplit;
+  g.n_groups = p.n_groups;
+  g.m_groups = p.m_groups;
+  // every tile must fall in a range of at most NTG tiles
+  if (p.n_groups < 1 || (g.W.n_tiles + p.n_groups - 1) / p.n_groups > p.ntg) return hipErrorInvalidValue;
+  if (p.rowmajor) {
+    if constexpr (EPI == EPI_FC || EPI == EPI_KV || EPI == EPI_PART)
+      return launch_fixed<T, EPI, true, false>(p, g, e, s);
+    return hipErrorInvalidValue;
+  }
+  if constexpr (EPI == EPI_FC || EPI == EPI_KV) {
+    if constexpr (sizeof(T) == 2) {
+      if (p.split) return launch_fixed<T, EPI, false, true>(p, g, e, s);
+    }
+    return launch_fixed<T, EPI, false, false>(p, g, e, s);
+  } else {
+    if constexpr (sizeof(T) == 2) {
+      if (p.split) return launch_hot<T, EPI, false, true>(p, g, e, s);
+    }
+    return launch_hot<T, EPI, false, false>(p, g, e, s);
+  }
+}
+
+}  // namespace dflash

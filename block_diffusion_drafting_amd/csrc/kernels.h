@@ -99,6 +99,9 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
 template <typename T>
 hipError_t launch_gemm(int epi, const GemmPlan& p, const GemmArgs& g, const EpiArgs& e,
                        hipStream_t s);
+// One epilogue's compiled variants (defined in gemm_kernel.h).
+template <typename T, int EPI>
+hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 
 struct AttnArgs {
   const void* q;

@@ -208,7 +208,9 @@ dflash_status dflash_ctx_buffers(const dflash_ctx *c, int32_t b, const void **ct
                                  int32_t *phys_rows);
 
 /* Per-kernel timing with HIP events recorded on the call's stream around
- * every launch of dflash_project_ctx / dflash_draft_block while enabled.
+ * every launch of dflash_project_ctx / dflash_draft_block that belongs to a
+ * phase selected by dflash_profile_enable (bit p of phase_mask selects phase
+ * p; 0 turns timing off; bits past the last phase are ignored).
  * Phases (index: name): 0 embed, 1 qkv, 2 attention, 3 o_proj, 4 gate_up,
  * 5 down, 6 lm_head, 7 finalize, 8 fc, 9 kv_inject, 10 grow, 11 rowmap,
  * 12 attn_combine, 13 resid_norm, 14 fc_finalize.
@@ -216,7 +218,7 @@ dflash_status dflash_ctx_buffers(const dflash_ctx *c, int32_t b, const void **ct
  * (milliseconds) and launch counts per phase into ms[] / count[] (host
  * arrays of DFLASH_NUM_PHASES entries, overwritten) and clears the record. */
 #define DFLASH_NUM_PHASES 15
-dflash_status dflash_profile_enable(dflash_ctx *c, int32_t enable);
+dflash_status dflash_profile_enable(dflash_ctx *c, uint32_t phase_mask);
 dflash_status dflash_profile_read(dflash_ctx *c, double *ms, int64_t *count);
 const char *dflash_phase_name(int32_t phase);
 
