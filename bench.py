@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--K", type=int, default=0, help="override the block size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-steps", type=int, default=25)
     ap.add_argument("--ksweep", action="store_true")
     ap.add_argument("--draft-iters", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -295,7 +295,7 @@ def main():
                                           / HBM_PEAK_GBS, 4),
             "step_hbm_frac": round(byt / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "phase_ms_per_step": phases,
-            "roofline": {"kernel": "lm_head GEMM + argmax (gemm_skinny, EPI_ARGMAX)",
+            "roofline": {"kernel": "LM head product + argmax (gemm_kernel, EPI_ARGMAX)",
                          "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(), "avg_launch_ms": round(lm_avg, 5),
