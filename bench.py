@@ -70,10 +70,11 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload: str, K: int):
     """HBM bytes per LM-head launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
-    the summary is missing or the kernel sources changed since."""
+    the summary is missing, was taken on another workload, or the kernel
+    sources changed since."""
     try:
         vals = {}
         with open(TRAFFIC_FILE) as f:
@@ -82,6 +83,8 @@ def measured_traffic():
                     k, v = line.split(":", 1)
                     vals[k.strip()] = v.strip()
         if vals.get("source_sha256") != kernel_source_hash():
+            return None
+        if vals.get("workload") != f"{workload} K={K}":
             return None
         return int(vals["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -229,8 +232,15 @@ def main():
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / args.steps
             byt = block_bytes(wl.shape, mb, lens0, K, wl.batch)
+            # per-phase times of a separate profiled pass
+            ctx.profile(True)
+            for _ in range(3):
+                dfl.dflash_draft_block(ctx, ids0, K, draft)
+            ph = {k: round(v[0] / 3, 4) for k, v in ctx.profile_read().items()}
+            ctx.profile(False)
             results.append({"K": K, "draft_accept_ms": round(ms, 4), "draft_block_ms": round(draft_ms, 4),
-                            "hbm_frac": round(byt / (draft_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                            "hbm_frac": round(byt / (draft_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "phase_ms": ph})
             log(f"[bench] K={K}: draft+accept {ms:.3f} ms, draft {draft_ms:.3f} ms")
             continue
 
@@ -298,7 +308,7 @@ def main():
             "roofline": {"kernel": "LM head product + argmax (gemm_kernel, EPI_ARGMAX)",
                          "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(), "avg_launch_ms": round(lm_avg, 5),
+                         "traffic": measured_traffic(wl.name, K), "avg_launch_ms": round(lm_avg, 5),
                          "bytes_per_launch": lm_bytes},
         }
         if not args.no_cpu_baseline:

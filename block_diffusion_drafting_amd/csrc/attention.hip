@@ -57,11 +57,16 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, col = lane & 15;
-  int u = blockIdx.x;
+  // Workgroups of the same (sequence, KV head, split) and different query
+  // groups read the same keys; blocks are dealt to the 8 XCDs round-robin,
+  // so they are numbered to share blockIdx % 8 (one L2) -- see attn_grid.
+  const int lo = blockIdx.x & 7;
+  const int rest = blockIdx.x >> 3;
+  const int qg = rest % a.qgroups;
+  int u = (rest / a.qgroups) * 8 + lo;
+  if (u >= a.B * a.nkv * a.max_splits) return;
   const int s = u % a.max_splits;
   u /= a.max_splits;
-  const int qg = u % a.qgroups;
-  u /= a.qgroups;
   const int g = u % a.nkv;
   const int b = u / a.nkv;
 
@@ -338,9 +343,16 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out
   frag_store<T, 4>(out, b * a.K + i, h * D + t * 16 + g4 * 4, v);
 }
 
+// (sequence, KV head, split) units padded to a multiple of 8, times the
+// query groups
+static unsigned attn_grid(const AttnArgs& a) {
+  const unsigned units = (unsigned)a.B * a.nkv * a.max_splits;
+  return (units + 7u) / 8u * 8u * (unsigned)a.qgroups;
+}
+
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)a.B * a.nkv * a.qgroups * a.max_splits);
+  dim3 grid(attn_grid(a));
   switch (a.d) {
     case 64: hipLaunchKernelGGL((attention_kernel<T, 64>), grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL((attention_kernel<T, 128>), grid, dim3(256), 0, s, a); break;

@@ -15,19 +15,22 @@ namespace dflash {
 // loses bandwidth; measured on the Qwen3-4B-shaped phases on MI355X.
 constexpr int kCUs = 256;
 
-// tiles-per-workgroup variants compiled for each m-tile count
+// tiles-per-workgroup variants compiled for each m-tile count, and the
+// largest one used: with many activation rows a workgroup re-reads every row
+// for its tiles, so wider tile ranges cut that traffic (accumulators of up to
+// 40 tiles live in the accumulation registers)
 static int round_ntg(int mtt, int want) {
   static const int v1[] = {1, 2, 4, 5, 6, 8};
-  static const int v2[] = {1, 2, 4, 8};
-  static const int v4[] = {1, 2, 4};
-  static const int v8[] = {1, 2};
+  static const int v2[] = {1, 2, 4, 5, 8};
+  static const int v4[] = {1, 2, 4, 5, 8};
+  static const int v8[] = {1, 2, 4, 5};
   const int* v = mtt == 1 ? v1 : mtt == 2 ? v2 : mtt == 4 ? v4 : v8;
-  const int n = mtt == 1 ? 6 : mtt == 2 ? 4 : mtt == 4 ? 3 : 2;
+  const int n = mtt == 1 ? 6 : mtt == 8 ? 4 : 5;
   for (int i = 0; i < n; ++i)
     if (v[i] >= want) return v[i];
   return v[n - 1];
 }
-static int max_ntg(int mtt) { return mtt == 1 ? 8 : mtt == 2 ? 8 : mtt == 4 ? 4 : 2; }
+static int max_ntg(int mtt) { return mtt == 8 ? 5 : 8; }
 
 // the project-path products (context projection and K/V injection) keep a
 // fixed shape: they run once per step over few rows or once at prefill

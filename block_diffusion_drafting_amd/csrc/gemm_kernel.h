@@ -169,17 +169,23 @@ __device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 a
 // ---------------------------------------------------------------------------
 // the product kernel
 // ---------------------------------------------------------------------------
-// Activation fragment(s) of m-tile mt, k-block kb (zero outside the matrix).
+// Activation fragment(s) of m-tile mt, k-block kb; zero when !ok or outside
+// the matrix.  `ok` and the m-tile test are wave-uniform (scalar branches);
+// the row test of the row-major form is per lane and uses a select.
 template <typename T, bool ROW, bool SPLIT>
-__device__ __forceinline__ void load_x(const GemmArgs& g, int mt, int kb, int lane, u32x4& hi,
+__device__ __forceinline__ void load_x(const GemmArgs& g, int mt, int kb, bool ok, int lane, u32x4& hi,
                                        u32x4& lo) {
   using E = Elem<T>;
   hi = u32x4{0u, 0u, 0u, 0u};
   lo = u32x4{0u, 0u, 0u, 0u};
+  if (!ok) return;
   if constexpr (ROW) {
-    const int row = mt * 16 + (lane & 15);
+    const int row0 = mt * 16 + (lane & 15);
+    const int row = min(row0, g.M - 1);
     const int k = kb * E::KB + (lane >> 4) * E::KPL;
-    if (row < g.M && k < g.W.kd) hi = *(const u32x4*)((const T*)g.Xrow + (size_t)row * g.ldx + k);
+    const u32x4 v = gld16((const T*)g.Xrow + (size_t)row * g.ldx + k);
+    const uint32_t keep = row0 < g.M ? 0xFFFFFFFFu : 0u;
+    hi = v & keep;
   } else {
     if (mt < g.X.mtiles) {
       const size_t slot = ((size_t)mt * g.X.nkb + kb) * WAVE + lane;
@@ -199,16 +205,20 @@ struct DefaultChk {
 };
 
 template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT, int WAVES = 4,
-          int CHK = DefaultChk<MTT, NTG, SPLIT>::value>
+          int CHK = DefaultChk<MTT, NTG, SPLIT>::value, bool PIPE = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e) {
   using E = Elem<T>;
   constexpr int ITEMS = NTG * MTT;
-  __shared__ f32x4 red[WAVES][ITEMS][WAVE];
+  // the waves' sums are added through LDS in rounds of RB output tiles
+  constexpr int RB = ITEMS < 64 / WAVES ? ITEMS : 64 / WAVES;
+  __shared__ f32x4 red[WAVES][RB][WAVE];
   __shared__ unsigned long long kmax[MTT][16];
   __shared__ float rnorm[MTT * 16];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform values held in scalar registers, so that the batch loop's
+  // branches are scalar and the loads are never under an exec mask
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int u = blockIdx.x;
   const int s = u % g.nsplit;
   u /= g.nsplit;
@@ -216,18 +226,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
   const int mg = u / g.n_groups;
   // balanced tile ranges: group ng owns tiles [tile0, tile0 + nt), nt <= NTG
   const int tile0 = (int)((long)ng * g.W.n_tiles / g.n_groups);
-  const int nt = (int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0;
+  const int nt = __builtin_amdgcn_readfirstlane((int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0);
   const int mt0 = mg * MTT;
   const int kbA = s * g.kbu;
   const int kbB = min(g.W.nkb, kbA + g.kbu);
   const int per = (kbB - kbA + WAVES - 1) / WAVES;
-  const int kw0 = kbA + wave * per;
-  const int kw1 = min(kbB, kw0 + per);
+  const int kw0 = __builtin_amdgcn_readfirstlane(kbA + wave * per);
+  const int kw1 = __builtin_amdgcn_readfirstlane(min(kbB, kw0 + per));
 
   const uint8_t* wb[NTG];
 #pragma unroll
   for (int t = 0; t < NTG; ++t) {
-    const int tile = min(tile0 + t, g.W.n_tiles - 1);   // out-of-range tiles: read a valid one, never stored
+    const int tile = tile0 + min(t, nt - 1);   // slots past the range re-read its last tile, never used
     wb[t] = g.W.w + (size_t)tile * g.W.nkb * BLOCK_BYTES + lane * FRAG_BYTES;
   }
   f32x4 acc[NTG][MTT];
@@ -243,29 +253,53 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
     }
   }
 
-  for (int kb = kw0; kb < kw1; kb += CHK) {
+  // One batch: CHK k-blocks of weight fragments (HBM) and the matching
+  // activation fragments (L2), then the MFMAs.
+  struct Batch {
     u32x4 wf[NTG][CHK];
     u32x4 xh[MTT][CHK], xl[MTT][CHK];
+  };
+  // Full batches (every tile of the group, every k-block in the wave's range,
+  // every m-tile present) load unconditionally, so the waits before the
+  // MFMAs count exactly the loads they need; the other batches test each
+  // fragment (uniform conditions: scalar branches).
+  auto load_full = [&](Batch& b, int kb) {
+#pragma unroll
+    for (int j = 0; j < CHK; ++j)
+#pragma unroll
+      for (int t = 0; t < NTG; ++t)
+        b.wf[t][j] = __builtin_nontemporal_load((const u32x4*)(wb[t] + (size_t)(kb + j) * BLOCK_BYTES));
+#pragma unroll
+    for (int j = 0; j < CHK; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MTT; ++mt) {
+        if constexpr (ROW) {
+          load_x<T, ROW, SPLIT>(g, mt0 + mt, kb + j, true, lane, b.xh[mt][j], b.xl[mt][j]);
+        } else {
+          const size_t slot = ((size_t)(mt0 + mt) * g.X.nkb + kb + j) * WAVE + lane;
+          b.xh[mt][j] = g.X.hi[slot];
+          if constexpr (SPLIT) b.xl[mt][j] = g.X.lo[slot];
+        }
+      }
+  };
+  auto load_part = [&](Batch& b, int kb) {
 #pragma unroll
     for (int j = 0; j < CHK; ++j) {
       const bool ok = kb + j < kw1;
 #pragma unroll
       for (int t = 0; t < NTG; ++t)
-        wf[t][j] = (ok && t < nt)
-                       ? __builtin_nontemporal_load((const u32x4*)(wb[t] + (size_t)(kb + j) * BLOCK_BYTES))
-                       : u32x4{0u, 0u, 0u, 0u};
+        b.wf[t][j] = (ok && t < nt)
+                         ? __builtin_nontemporal_load((const u32x4*)(wb[t] + (size_t)(kb + j) * BLOCK_BYTES))
+                         : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < CHK; ++j) {
       const bool ok = kb + j < kw1;
 #pragma unroll
-      for (int mt = 0; mt < MTT; ++mt) {
-        if (ok)
-          load_x<T, ROW, SPLIT>(g, mt0 + mt, kb + j, lane, xh[mt][j], xl[mt][j]);
-        else
-          xh[mt][j] = xl[mt][j] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int mt = 0; mt < MTT; ++mt) load_x<T, ROW, SPLIT>(g, mt0 + mt, kb + j, ok, lane, b.xh[mt][j], b.xl[mt][j]);
     }
+  };
+  auto compute = [&](const Batch& b) {
 #pragma unroll
     for (int j = 0; j < CHK; ++j)
 #pragma unroll
@@ -273,28 +307,69 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
         if (t >= nt) continue;   // uniform over the workgroup
 #pragma unroll
         for (int mt = 0; mt < MTT; ++mt) {
-          acc[t][mt] = E::mma(wf[t][j], xh[mt][j], acc[t][mt]);
-          if constexpr (SPLIT) acc[t][mt] = E::mma(wf[t][j], xl[mt][j], acc[t][mt]);
+          acc[t][mt] = E::mma(b.wf[t][j], b.xh[mt][j], acc[t][mt]);
+          if constexpr (SPLIT) acc[t][mt] = E::mma(b.wf[t][j], b.xl[mt][j], acc[t][mt]);
         }
       }
+  };
+  const bool full_group = nt == NTG && (ROW || mt0 + MTT <= g.X.mtiles);
+  const int nfull = full_group ? (kw1 - kw0) / CHK : 0;
+  int kb = kw0;
+  if constexpr (PIPE) {
+    // two batches in flight: batch i+1 loads while batch i computes (the
+    // last iteration re-loads a batch it does not use, so that every load
+    // stays unconditional)
+    if (nfull > 0) {
+      Batch b0, b1;
+      load_full(b0, kb);
+      int i = 0;
+      for (; i + 2 <= nfull; i += 2) {
+        load_full(b1, kb + CHK);
+        compute(b0);
+        load_full(b0, kb + (i + 2 < nfull ? 2 * CHK : CHK));
+        compute(b1);
+        kb += 2 * CHK;
+      }
+      if (i < nfull) {
+        compute(b0);
+        kb += CHK;
+      }
+    }
+  } else {
+    for (int i = 0; i < nfull; ++i, kb += CHK) {
+      Batch b;
+      load_full(b, kb);
+      compute(b);
+    }
+  }
+  for (; kb < kw1; kb += CHK) {
+    Batch b;
+    load_part(b, kb);
+    compute(b);
   }
 
-  // add the waves' sums in wave order
-#pragma unroll
-  for (int t = 0; t < NTG; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MTT; ++mt) red[wave][t * MTT + mt][lane] = acc[t][mt];
+  // add the waves' sums in wave order, RB tiles per round
   if constexpr (EPI == EPI_ARGMAX) {
     if (threadIdx.x < MTT * 16) (&kmax[0][0])[threadIdx.x] = 0ull;
   }
-  __syncthreads();
-  for (int it = wave; it < nt * MTT; it += WAVES) {
-    const int t = it / MTT, mt = it % MTT;
-    const int tile = tile0 + t;
-    f32x4 sum = red[0][it][lane];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][it][lane];
-    epilogue_tile<T, EPI>(e, s, tile, mt0 + mt, sum, lane, rnorm[mt * 16 + (lane & 15)], kmax[mt]);
+  for (int r0 = 0; r0 < ITEMS; r0 += RB) {
+    if (r0 >= nt * MTT) break;   // uniform over the workgroup
+    if (r0 > 0) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int it = r0 + i;
+      if (it < ITEMS) red[wave][i][lane] = acc[it / MTT][it % MTT];
+    }
+    __syncthreads();
+    for (int i = wave; i < RB && r0 + i < nt * MTT; i += WAVES) {
+      const int it = r0 + i;
+      const int t = it / MTT, mt = it % MTT;
+      f32x4 sum = red[0][i][lane];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][i][lane];
+      epilogue_tile<T, EPI>(e, s, tile0 + t, mt0 + mt, sum, lane, rnorm[mt * 16 + (lane & 15)], kmax[mt]);
+    }
   }
   if constexpr (EPI == EPI_ARGMAX) {
     __syncthreads();
@@ -319,56 +394,63 @@ struct HotChk {
   static constexpr int value = C < 1 ? 1 : C;
 };
 
-template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT, int WAVES, int CHK>
+template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT, int WAVES, int CHK,
+          bool PIPE = false>
 inline hipError_t launch_v(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   dim3 grid((unsigned)p.n_groups * p.m_groups * p.nsplit);
-  hipLaunchKernelGGL((gemm_kernel<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK>), grid, dim3(WAVES * 64), 0, s, g,
-                     e);
+  hipLaunchKernelGGL((gemm_kernel<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>), grid, dim3(WAVES * 64), 0,
+                     s, g, e);
   return hipGetLastError();
 }
 
 template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT>
 inline hipError_t launch_h(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  // one m-tile: eight waves stream; more m-tiles: four waves (one per SIMD,
+  // large accumulator sets) with the next load batch in flight during the
+  // MFMAs of the current one
+  // (two batches in registers: half the batch size)
   constexpr int WAVES = MTT == 1 ? 8 : 4;
-  return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, HotChk<MTT, NTG, SPLIT>::value>(p, g, e, s);
+  constexpr bool PIPE = MTT > 1;
+  constexpr int CHK = PIPE ? (HotChk<MTT, NTG, SPLIT>::value + 1) / 2 : HotChk<MTT, NTG, SPLIT>::value;
+  return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>(p, g, e, s);
+}
+
+// bf16 products use the hi/lo activation pair exactly when a workgroup holds
+// at most two m-tiles; only those combinations are compiled
+template <typename T, int MTT, bool SPLIT>
+constexpr bool compiled() {
+  return sizeof(T) == 4 ? !SPLIT : (SPLIT == (MTT <= 2));
+}
+
+template <typename T, int MTT, int EPI, bool ROW, bool SPLIT>
+inline hipError_t launch_mtt(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  if constexpr (!compiled<T, MTT, SPLIT>()) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (p.ntg) {
+      case 1: return launch_h<T, MTT, 1, EPI, ROW, SPLIT>(p, g, e, s);
+      case 2: return launch_h<T, MTT, 2, EPI, ROW, SPLIT>(p, g, e, s);
+      case 4: return launch_h<T, MTT, 4, EPI, ROW, SPLIT>(p, g, e, s);
+      case 5: return launch_h<T, MTT, 5, EPI, ROW, SPLIT>(p, g, e, s);
+    }
+    if constexpr (MTT == 1) {
+      if (p.ntg == 6) return launch_h<T, MTT, 6, EPI, ROW, SPLIT>(p, g, e, s);
+    }
+    if constexpr (MTT <= 4) {
+      if (p.ntg == 8) return launch_h<T, MTT, 8, EPI, ROW, SPLIT>(p, g, e, s);
+    }
+    return hipErrorInvalidValue;
+  }
 }
 
 template <typename T, int EPI, bool ROW, bool SPLIT>
 inline hipError_t launch_hot(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
   switch (p.mtt) {
-    case 1:
-      switch (p.ntg) {
-        case 1: return launch_h<T, 1, 1, EPI, ROW, SPLIT>(p, g, e, s);
-        case 2: return launch_h<T, 1, 2, EPI, ROW, SPLIT>(p, g, e, s);
-        case 4: return launch_h<T, 1, 4, EPI, ROW, SPLIT>(p, g, e, s);
-        case 5: return launch_h<T, 1, 5, EPI, ROW, SPLIT>(p, g, e, s);
-        case 6: return launch_h<T, 1, 6, EPI, ROW, SPLIT>(p, g, e, s);
-        case 8: return launch_h<T, 1, 8, EPI, ROW, SPLIT>(p, g, e, s);
-      }
-      break;
-    case 2:
-      switch (p.ntg) {
-        case 1: return launch_h<T, 2, 1, EPI, ROW, SPLIT>(p, g, e, s);
-        case 2: return launch_h<T, 2, 2, EPI, ROW, SPLIT>(p, g, e, s);
-        case 4: return launch_h<T, 2, 4, EPI, ROW, SPLIT>(p, g, e, s);
-        case 8: return launch_h<T, 2, 8, EPI, ROW, SPLIT>(p, g, e, s);
-      }
-      break;
-    case 4:
-      switch (p.ntg) {
-        case 1: return launch_h<T, 4, 1, EPI, ROW, SPLIT>(p, g, e, s);
-        case 2: return launch_h<T, 4, 2, EPI, ROW, SPLIT>(p, g, e, s);
-        case 4: return launch_h<T, 4, 4, EPI, ROW, SPLIT>(p, g, e, s);
-      }
-      break;
-    default:
-      switch (p.ntg) {
-        case 1: return launch_h<T, 8, 1, EPI, ROW, SPLIT>(p, g, e, s);
-        case 2: return launch_h<T, 8, 2, EPI, ROW, SPLIT>(p, g, e, s);
-      }
-      break;
+    case 1: return launch_mtt<T, 1, EPI, ROW, SPLIT>(p, g, e, s);
+    case 2: return launch_mtt<T, 2, EPI, ROW, SPLIT>(p, g, e, s);
+    case 4: return launch_mtt<T, 4, EPI, ROW, SPLIT>(p, g, e, s);
+    default: return launch_mtt<T, 8, EPI, ROW, SPLIT>(p, g, e, s);
   }
-  return hipErrorInvalidValue;
 }
 
 template <typename T, int EPI, bool ROW, bool SPLIT>
