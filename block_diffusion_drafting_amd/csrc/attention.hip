@@ -35,8 +35,8 @@ size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d) {
   return (size_t)B * nkv * qgroups * max_splits * 4 * (d * 16 + 32);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+template <typename T, int D, int QG>
+__global__ __launch_bounds__(256 * QG) void attention_kernel(AttnArgs a) {
   using E = Elem<T>;
   constexpr int CHUNK_KEYS = chunk_keys<T, D>();
   constexpr int ES = sizeof(T);
@@ -50,20 +50,24 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   constexpr int VP_ROW = CHUNK_KEYS * ES / 16;          // 16-byte pieces per V^T row
   constexpr int VPIECES = D * VP_ROW;
   constexpr int EPP = 16 / ES;                          // keys per V^T piece
-  constexpr int KPT = KPIECES / 256, VPT = VPIECES / 256;
-  static_assert(KPIECES % 256 == 0 && VPIECES % 256 == 0, "chunk staging");
+  constexpr int NTH = 256 * QG;   // threads of the workgroup
+  constexpr int KPT = KPIECES / NTH, VPT = VPIECES / NTH;
+  static_assert(KPIECES % NTH == 0 && VPIECES % NTH == 0, "chunk staging");
   __shared__ __attribute__((aligned(16))) uint8_t kl[2][CHUNK_KEYS * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t vl[2][D * VROW];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // QG query groups share each staged chunk: wave w is query tile w % 4 of
+  // query group qgp * QG + w / 4
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   const int g4 = lane >> 4, col = lane & 15;
   // Workgroups of the same (sequence, KV head, split) and different query
   // groups read the same keys; blocks are dealt to the 8 XCDs round-robin,
   // so they are numbered to share blockIdx % 8 (one L2) -- see attn_grid.
+  const int nqgp = (a.qgroups + QG - 1) / QG;
   const int lo = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
-  const int qg = rest % a.qgroups;
-  int u = (rest / a.qgroups) * 8 + lo;
+  const int qg = (rest % nqgp) * QG + (int)(threadIdx.x >> 8);
+  int u = (rest / nqgp) * 8 + lo;
   if (u >= a.B * a.nkv * a.max_splits) return;
   const int s = u % a.max_splits;
   u /= a.max_splits;
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   const int nrows = a.K * rep;
   const int qt = qg * 4 + wave;
   const int r = qt * 16 + col;
-  const bool row_ok = r < nrows;
+  const bool row_ok = qg < a.qgroups && r < nrows;
   const int h = g * rep + (row_ok ? r / a.K : 0);
   const int i = row_ok ? r % a.K : 0;
   u32x4 qf[NFD];
@@ -122,14 +126,14 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   auto gload = [&](int c0, int cend) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int t = threadIdx.x + j * 256;
+      const int t = threadIdx.x + j * NTH;
       const int row = t / KP_ROW, pc = t % KP_ROW;
       kr[j] = (c0 + row < cend) ? gld16((const uint8_t*)(kbase + (size_t)(c0 + row) * D) + pc * 16)
                                 : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int t = threadIdx.x + j * 256;
+      const int t = threadIdx.x + j * NTH;
       const int dr = t / VP_ROW, pc = t % VP_ROW;
       const int key = c0 + pc * EPP;
       const T* src = vbase + (size_t)dr * vstride + key;
@@ -148,12 +152,12 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int t = threadIdx.x + j * 256;
+      const int t = threadIdx.x + j * NTH;
       *(u32x4*)(kl[buf] + (t / KP_ROW) * KROW + (t % KP_ROW) * 16) = kr[j];
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int t = threadIdx.x + j * 256;
+      const int t = threadIdx.x + j * NTH;
       *(u32x4*)(vl[buf] + (t / VP_ROW) * VROW + (t % VP_ROW) * 16) = vr[j];
     }
   };
@@ -246,6 +250,7 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
 
   // o[t][j] = O^T[d = 16t + 4*g4 + j][query column col]; every split writes
   // its partial (m, l, O); attn_combine merges them in split order.
+  if (qg >= a.qgroups) return;   // padding query group of an odd count
   const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
   const size_t wstride = (size_t)D * 16 + 32;
   float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
@@ -344,18 +349,23 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out
 }
 
 // (sequence, KV head, split) units padded to a multiple of 8, times the
-// query groups
-static unsigned attn_grid(const AttnArgs& a) {
+// workgroups of query groups (QG per workgroup)
+static unsigned attn_grid(const AttnArgs& a, int qg_per_wg) {
   const unsigned units = (unsigned)a.B * a.nkv * a.max_splits;
-  return (units + 7u) / 8u * 8u * (unsigned)a.qgroups;
+  return (units + 7u) / 8u * 8u * (unsigned)((a.qgroups + qg_per_wg - 1) / qg_per_wg);
 }
 
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(attn_grid(a));
-  switch (a.d) {
-    case 64: hipLaunchKernelGGL((attention_kernel<T, 64>), grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((attention_kernel<T, 128>), grid, dim3(256), 0, s, a); break;
+  // two query groups per workgroup (eight waves) whenever there are several:
+  // each staged K/V chunk then serves 128 query rows
+  const int QG = a.qgroups > 1 ? 2 : 1;
+  dim3 grid(attn_grid(a, QG));
+  switch (a.d * 4 + QG) {
+    case 64 * 4 + 1: hipLaunchKernelGGL((attention_kernel<T, 64, 1>), grid, dim3(256), 0, s, a); break;
+    case 64 * 4 + 2: hipLaunchKernelGGL((attention_kernel<T, 64, 2>), grid, dim3(512), 0, s, a); break;
+    case 128 * 4 + 1: hipLaunchKernelGGL((attention_kernel<T, 128, 1>), grid, dim3(256), 0, s, a); break;
+    case 128 * 4 + 2: hipLaunchKernelGGL((attention_kernel<T, 128, 2>), grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -405,13 +405,14 @@ inline hipError_t launch_v(const GemmPlan& p, const GemmArgs& g, const EpiArgs& 
 
 template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT>
 inline hipError_t launch_h(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  // one m-tile: eight waves stream; more m-tiles: four waves (one per SIMD,
-  // large accumulator sets) with the next load batch in flight during the
-  // MFMAs of the current one
-  // (two batches in registers: half the batch size)
-  constexpr int WAVES = MTT == 1 ? 8 : 4;
-  constexpr bool PIPE = MTT > 1;
-  constexpr int CHK = PIPE ? (HotChk<MTT, NTG, SPLIT>::value + 1) / 2 : HotChk<MTT, NTG, SPLIT>::value;
+  // one m-tile: eight waves stream; two or four m-tiles: four waves (one
+  // per SIMD, large accumulator sets) with the next load batch in flight
+  // during the MFMAs of the current one
+  // (two batches in registers: half the batch size).  Eight m-tiles: eight
+  // waves of single batches measured faster than four pipelined waves.
+  constexpr int WAVES = MTT == 1 || MTT == 8 ? 8 : 4;
+  constexpr bool PIPE = MTT == 2 || MTT == 4;
+  constexpr int CHK = MTT > 1 ? (HotChk<MTT, NTG, SPLIT>::value + 1) / 2 : HotChk<MTT, NTG, SPLIT>::value;
   return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>(p, g, e, s);
 }
 
