@@ -561,21 +561,29 @@ static dflash_status project_impl(dflash_ctx* c, const void* feats, const int32_
   if ((st = ensure(c->alloc, c->rowmap, sizeof(RowMap) * total)) ||
       (st = ensure_frag(c, c->c_hi, c->c_lo, sizeof(T) == 2, mtiles, m->fc.n_tiles * 16 * m->es / 64, s, cb)))
     return st;
-  {
-    PhaseTimer tm(c, PH_ROWMAP, s);
-    HIP_TRY(launch_rowmap(start.data(), B, total, positions, c->seq_dev, (RowMap*)c->rowmap.p, s));
+  RowInfo ri;
+  for (int b = 0; b < B; ++b) {
+    ri.start[b] = start[b];
+    ri.ctx0[b] = c->seq[b].ctx_len;
   }
+  ri.start[B] = start[B];
   EpiArgs e = base_epi(c, total);
   e.cbuf = cb;
   e.rowmap = (const RowMap*)c->rowmap.p;
   const Frag none{};
   if (mtiles <= 4) {
     // few rows: split the reduction over workgroups, then add the splits
+    // (and map the rows) in one pass
     GemmPlan p;
     if ((st = run_gemm<T>(c, PH_FC, EPI_PART, m->fc, none, feats, m->cfg.n_feat * H, total, e, s, &p))) return st;
     PhaseTimer tm(c, PH_FCFIN, s);
-    HIP_TRY(launch_fc_finalize<T>((const float*)c->part.p, p.nsplit, mtiles, total, H, e.rowmap, c->seq_dev, cb, s));
+    HIP_TRY(launch_fc_finalize<T>((const float*)c->part.p, p.nsplit, mtiles, total, H, ri, B, positions,
+                                  (RowMap*)c->rowmap.p, c->seq_dev, cb, s));
   } else {
+    {
+      PhaseTimer tm(c, PH_ROWMAP, s);
+      HIP_TRY(launch_rowmap(ri, B, total, positions, c->seq_dev, (RowMap*)c->rowmap.p, s));
+    }
     if ((st = run_gemm<T>(c, PH_FC, EPI_FC, m->fc, none, feats, m->cfg.n_feat * H, total, e, s))) return st;
   }
   if (m->cfg.n_layers > 0)
@@ -632,17 +640,22 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   const int rep = nq / nkv;
   const int qtiles = (K * rep + 15) / 16;
   const int qgroups = (qtiles + 3) / 4;
-  int64_t work = 0;
   int max_len = 0;
-  for (int b = 0; b < B; ++b) {
-    work += (int64_t)(c->seq[b].ctx_len + K) * nkv * qgroups;
-    max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
+  for (int b = 0; b < B; ++b) max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
+  // Keys per split: the smallest multiple of 64, at least 128, whose
+  // workgroups fit one round of the chip (two 4-wave workgroups or one
+  // 8-wave workgroup per CU); at short contexts the split count, not the
+  // split length, sets the cost of the combine.
+  const int qg_per_wg = qgroups > 1 ? 2 : 1;
+  const int64_t wg_per_split = (int64_t)nkv * ((qgroups + qg_per_wg - 1) / qg_per_wg);
+  const int64_t round_wgs = qg_per_wg == 1 ? 512 : 256;
+  int chunk = 128;
+  for (;; chunk += 64) {
+    int64_t wgs = 0;
+    for (int b = 0; b < B; ++b)
+      wgs += wg_per_split * ((c->seq[b].ctx_len + chunk - 1) / chunk + (K + chunk - 1) / chunk);
+    if (wgs <= round_wgs || chunk >= max_len + K) break;
   }
-  // keys per split: a multiple of 64 giving about 512 workgroups, and at
-  // least 128 (at short contexts the split count, not the chunk size, sets
-  // the cost of the combine)
-  int chunk = 64 * (int)((work + 64 * 512 - 1) / (64 * 512));
-  if (chunk < 128) chunk = 128;
   const int max_splits = (max_len + chunk - 1) / chunk + (K + chunk - 1) / chunk;
   if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d) * sizeof(float))))
     return st;

@@ -32,10 +32,13 @@ static int round_ntg(int mtt, int want) {
 }
 static int max_ntg(int mtt) { return mtt == 8 ? 5 : 8; }
 
-// the project-path products (context projection and K/V injection) keep a
-// fixed shape: they run once per step over few rows or once at prefill
-// (and so does a context projection split over k with row-major input)
-static bool fixed_shape(int epi, bool rowmajor) { return epi == EPI_FC || epi == EPI_KV || rowmajor; }
+// The context-path products keep a fixed shape at prefill sizes (more than
+// two m-tiles: they run once); the per-step ones (the accepted rows, at
+// most two m-tiles) use the balanced planning.  EPI_FC (the whole context
+// projection in one pass) is only used at prefill sizes.
+static bool fixed_shape(int epi, bool rowmajor, int mtt) {
+  return epi == EPI_FC || ((epi == EPI_KV || rowmajor) && mtt > 2);
+}
 static int fixed_ntg(int epi) { return epi == EPI_FC ? 4 : 2; }
 
 GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor) {
@@ -57,7 +60,8 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
     p.nsplit = 1;
     p.part_floats = 0;
   }
-  if (fixed_shape(epi, rowmajor)) {
+  p.fixed = fixed_shape(epi, rowmajor, p.mtt);
+  if (p.fixed) {
     p.ntg = fixed_ntg(epi);
     p.n_groups = (T + p.ntg - 1) / p.ntg;
     return p;

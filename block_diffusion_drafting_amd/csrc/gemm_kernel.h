@@ -416,16 +416,20 @@ inline hipError_t launch_h(const GemmPlan& p, const GemmArgs& g, const EpiArgs& 
   return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>(p, g, e, s);
 }
 
-// bf16 products use the hi/lo activation pair exactly when a workgroup holds
-// at most two m-tiles; only those combinations are compiled
-template <typename T, int MTT, bool SPLIT>
+// Compiled combinations: bf16 draft products use the hi/lo activation pair
+// exactly when a workgroup holds at most two m-tiles; the per-step context
+// products (row-major features, K/V injection) have at most two m-tiles,
+// and K/V injection always uses the pair for bf16.
+template <typename T, int MTT, int EPI, bool ROW, bool SPLIT>
 constexpr bool compiled() {
+  if constexpr (ROW) return !SPLIT && MTT <= 2;
+  if constexpr (EPI == EPI_KV) return MTT <= 2 && SPLIT == (sizeof(T) == 2);
   return sizeof(T) == 4 ? !SPLIT : (SPLIT == (MTT <= 2));
 }
 
 template <typename T, int MTT, int EPI, bool ROW, bool SPLIT>
 inline hipError_t launch_mtt(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  if constexpr (!compiled<T, MTT, SPLIT>()) {
+  if constexpr (!compiled<T, MTT, EPI, ROW, SPLIT>()) {
     return hipErrorInvalidValue;
   } else {
     switch (p.ntg) {
@@ -475,21 +479,27 @@ hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipS
   // every tile must fall in a range of at most NTG tiles
   if (p.n_groups < 1 || (g.W.n_tiles + p.n_groups - 1) / p.n_groups > p.ntg) return hipErrorInvalidValue;
   if (p.rowmajor) {
-    if constexpr (EPI == EPI_FC || EPI == EPI_KV || EPI == EPI_PART)
-      return launch_fixed<T, EPI, true, false>(p, g, e, s);
+    if constexpr (EPI == EPI_FC || EPI == EPI_KV || EPI == EPI_PART) {
+      if (p.fixed) return launch_fixed<T, EPI, true, false>(p, g, e, s);
+      if constexpr (EPI == EPI_PART) return launch_hot<T, EPI, true, false>(p, g, e, s);
+    }
     return hipErrorInvalidValue;
   }
   if constexpr (EPI == EPI_FC || EPI == EPI_KV) {
-    if constexpr (sizeof(T) == 2) {
-      if (p.split) return launch_fixed<T, EPI, false, true>(p, g, e, s);
+    if (p.fixed) {
+      if constexpr (sizeof(T) == 2) {
+        if (p.split) return launch_fixed<T, EPI, false, true>(p, g, e, s);
+      }
+      return launch_fixed<T, EPI, false, false>(p, g, e, s);
     }
-    return launch_fixed<T, EPI, false, false>(p, g, e, s);
-  } else {
+  }
+  if constexpr (EPI != EPI_FC) {
     if constexpr (sizeof(T) == 2) {
       if (p.split) return launch_hot<T, EPI, false, true>(p, g, e, s);
     }
     return launch_hot<T, EPI, false, false>(p, g, e, s);
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dflash

@@ -91,6 +91,7 @@ struct GemmPlan {
   int kbu, nsplit, n_groups, m_groups;
   bool split;  // use hi + lo fragments
   bool rowmajor;
+  bool fixed;  // fixed tile groups (the context path at prefill sizes)
   size_t part_floats;
 };
 
@@ -129,10 +130,18 @@ hipError_t launch_embed(const int32_t* ids, const void* embed, const float* gain
 template <typename T>
 hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
                              const float* gain, Frag xg, float* ssq, hipStream_t s);
-// c = sum of split-K partials -> context buffer rows + staging frag.
+// Rows of one context append: rows [start[b], start[b+1]) belong to
+// sequence b and go to slots ctx0[b] + (row - start[b]) (host values).
+struct RowInfo {
+  int32_t start[DFLASH_ROWMAP_MAX + 1];
+  int32_t ctx0[DFLASH_ROWMAP_MAX];
+};
+// c = sum of split-K partials -> context buffer rows + staging frag; also
+// writes the row map and advances the device context lengths.
 template <typename T>
-hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H,
-                              const RowMap* rowmap, const DevSeq* seqs, Frag cbuf, hipStream_t s);
+hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri, int B,
+                              const int32_t* positions, RowMap* rowmap, DevSeq* seqs, Frag cbuf,
+                              hipStream_t s);
 // draft ids from argmax keys; optional final-normed hidden rows.
 template <typename T>
 hipError_t launch_finalize(const unsigned long long* keys, int M, int32_t* draft, const float* x,
@@ -145,8 +154,8 @@ hipError_t launch_pack(const uint64_t* row_src, int n_rows_padded, int kd, int n
                        hipStream_t s);
 template <typename T>
 hipError_t launch_to_f32(const void* src, float* dst, int n, hipStream_t s);
-hipError_t launch_rowmap(const int32_t* row_start, int B, int total, const int32_t* positions,
-                         DevSeq* seqs, RowMap* out, hipStream_t s);
+hipError_t launch_rowmap(const RowInfo& ri, int B, int total, const int32_t* positions, DevSeq* seqs,
+                         RowMap* out, hipStream_t s);
 hipError_t launch_set_seq(DevSeq* seqs, int b, DevSeq v, hipStream_t s);
 template <typename T>
 hipError_t launch_grow_copy(DevSeq oldv, DevSeq newv, int L, int nkv, int d, int H,

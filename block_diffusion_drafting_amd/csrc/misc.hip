@@ -123,36 +123,59 @@ template hipError_t launch_resid_norm<float>(const float*, int, int, int, int, f
                                              Frag, float*, hipStream_t);
 
 // ---------------------------------------------------------------------------
-// (a1) context projection split over k: c = sum_s part_s, written to the
-// sequence's context buffer row (fp32) and to the frag staging that feeds
-// the KV injection product.
+// (a1)-(a2) context projection split over k: c = sum_s part_s, written to
+// the sequence's context buffer row (fp32) and to the frag staging that
+// feeds the KV injection product.  The row -> (sequence, slot, position) map
+// is computed here from the host's row starts and context lengths (passed
+// by value) and stored for the KV injection; block (0, 0) then advances the
+// device copy of every context length (nothing in this launch reads it).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ RowMap map_row(const RowInfo& ri, int B, int j, const int32_t* positions) {
+  int lo = 0, hi = B;  // b with start[b] <= j < start[b + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ri.start[mid] <= j) lo = mid; else hi = mid;
+  }
+  RowMap r;
+  r.b = lo;
+  r.slot = ri.ctx0[lo] + (j - ri.start[lo]);
+  r.pos = positions ? positions[j] : r.slot;
+  r.pad = 0;
+  return r;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void fc_finalize_kernel(const float* part, int nsplit, int mtiles,
-                                                          int M, int H, const RowMap* rowmap,
-                                                          const DevSeq* seqs, Frag cbuf) {
+                                                          int M, int H, RowInfo ri, int B,
+                                                          const int32_t* positions, RowMap* rowmap,
+                                                          DevSeq* seqs, Frag cbuf) {
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int b = threadIdx.x; b < B; b += blockDim.x) seqs[b].ctx_len = ri.ctx0[b] + ri.start[b + 1] - ri.start[b];
   const int m = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int n0 = blockIdx.y * 64 + (threadIdx.x & 15) * 4;
   if (m >= M) return;
+  const RowMap rm = map_row(ri, B, m, positions);
+  if (blockIdx.y == 0 && (threadIdx.x & 15) == 0) rowmap[m] = rm;
   const f32x4 c = sum_parts(part, nsplit, H / 16, mtiles, m, n0);
-  const RowMap rm = rowmap[m];
-  *(f32x4*)((float*)seqs[rm.b].ctxbuf + (size_t)rm.slot * H + n0) = c;
+  *gp((f32x4*)((float*)seqs[rm.b].ctxbuf + (size_t)rm.slot * H + n0)) = c;
   float v[4] = {c[0], c[1], c[2], c[3]};
   frag_store<T, 4>(cbuf, m, n0, v);
 }
 
 template <typename T>
-hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H,
-                              const RowMap* rowmap, const DevSeq* seqs, Frag cbuf, hipStream_t s) {
+hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri, int B,
+                              const int32_t* positions, RowMap* rowmap, DevSeq* seqs, Frag cbuf,
+                              hipStream_t s) {
+  if (B > DFLASH_ROWMAP_MAX) return hipErrorInvalidValue;
   dim3 grid((M + 15) / 16, H / 64);
-  hipLaunchKernelGGL((fc_finalize_kernel<T>), grid, dim3(256), 0, s, part, nsplit, mtiles, M, H,
-                     rowmap, seqs, cbuf);
+  hipLaunchKernelGGL((fc_finalize_kernel<T>), grid, dim3(256), 0, s, part, nsplit, mtiles, M, H, ri, B,
+                     positions, rowmap, seqs, cbuf);
   return hipGetLastError();
 }
-template hipError_t launch_fc_finalize<bf16_t>(const float*, int, int, int, int, const RowMap*,
-                                               const DevSeq*, Frag, hipStream_t);
-template hipError_t launch_fc_finalize<float>(const float*, int, int, int, int, const RowMap*,
-                                              const DevSeq*, Frag, hipStream_t);
+template hipError_t launch_fc_finalize<bf16_t>(const float*, int, int, int, int, const RowInfo&, int,
+                                               const int32_t*, RowMap*, DevSeq*, Frag, hipStream_t);
+template hipError_t launch_fc_finalize<float>(const float*, int, int, int, int, const RowInfo&, int,
+                                              const int32_t*, RowMap*, DevSeq*, Frag, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // (a9) end of the block: draft ids from the argmax keys; optionally the
@@ -275,38 +298,17 @@ template hipError_t launch_to_f32<float>(const void*, float*, int, hipStream_t);
 // position is positions[j] or that row.  Then ctx_len[b] += n_new[b].
 // One workgroup, so the reads of ctx_len precede the update.
 // ---------------------------------------------------------------------------
-struct RowStarts {
-  int32_t v[DFLASH_ROWMAP_MAX + 1];
-};
-
-__global__ __launch_bounds__(256) void rowmap_kernel(RowStarts st, int B, int total,
+__global__ __launch_bounds__(256) void rowmap_kernel(RowInfo ri, int B, int total,
                                                      const int32_t* positions, DevSeq* seqs,
                                                      RowMap* out) {
-  for (int j = threadIdx.x; j < total; j += blockDim.x) {
-    int lo = 0, hi = B;  // find b with st[b] <= j < st[b+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (st.v[mid] <= j) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    const int slot = seqs[b].ctx_len + (j - st.v[b]);
-    RowMap r;
-    r.b = b;
-    r.slot = slot;
-    r.pos = positions ? positions[j] : slot;
-    r.pad = 0;
-    out[j] = r;
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < B; b += blockDim.x) seqs[b].ctx_len += st.v[b + 1] - st.v[b];
+  for (int j = threadIdx.x; j < total; j += blockDim.x) out[j] = map_row(ri, B, j, positions);
+  for (int b = threadIdx.x; b < B; b += blockDim.x) seqs[b].ctx_len = ri.ctx0[b] + ri.start[b + 1] - ri.start[b];
 }
 
-hipError_t launch_rowmap(const int32_t* row_start, int B, int total, const int32_t* positions,
-                         DevSeq* seqs, RowMap* out, hipStream_t s) {
+hipError_t launch_rowmap(const RowInfo& ri, int B, int total, const int32_t* positions, DevSeq* seqs,
+                         RowMap* out, hipStream_t s) {
   if (B > DFLASH_ROWMAP_MAX) return hipErrorInvalidValue;
-  RowStarts st;
-  for (int b = 0; b <= B; ++b) st.v[b] = row_start[b];
-  hipLaunchKernelGGL(rowmap_kernel, dim3(1), dim3(256), 0, s, st, B, total, positions, seqs, out);
+  hipLaunchKernelGGL(rowmap_kernel, dim3(1), dim3(256), 0, s, ri, B, total, positions, seqs, out);
   return hipGetLastError();
 }
 
