@@ -3,8 +3,10 @@
 
 A step is one speculative step of the whole hot path for every sequence of
 the batch, enqueued on one stream with no host synchronisation:
-    dflash_draft_block (K block rows)  ->  dflash_accept  ->
-    dflash_project_ctx (the accepted positions of that step).
+    dflash_step (append the positions accepted at the previous step and
+    draft K block rows, one call)  ->  dflash_accept.
+The same work as three calls (dflash_draft_block -> dflash_accept ->
+dflash_project_ctx) is timed as well and reported beside it.
 The accepted counts come from the seeded stand-in verifier (they depend only
 on its agreement draws, so they are known ahead); its target tokens are
 pre-generated.  Inputs are resident in device memory before timing starts.
@@ -201,7 +203,8 @@ def main():
     stream = torch.cuda.current_stream()
     results = []
     for K in Ks:
-        steps = plan_steps(wl, K, args.warmup + args.steps)
+        steps = plan_steps(wl, K, (args.warmup + 2 * args.steps + 10) if not args.ksweep
+                           else args.warmup + args.steps)
         dev = [(torch.from_numpy(i).cuda(), torch.from_numpy(t).cuda(), tau, torch.from_numpy(f).cuda())
                for (i, t, tau, f) in steps]
         draft = torch.empty(wl.batch, K, dtype=torch.int32, device="cuda")
@@ -244,21 +247,42 @@ def main():
             log(f"[bench] K={K}: draft+accept {ms:.3f} ms, draft {draft_ms:.3f} ms")
             continue
 
-        def one(t):
+        # The production step: dflash_step appends the positions accepted
+        # at the previous step and drafts this block in one call (the
+        # context K/V written by the QKV products), then dflash_accept.
+        pending = [None]
+
+        def fused(t):
+            i, tg, tau, f = dev[t]
+            if pending[0] is None:
+                dfl.dflash_draft_block(ctx, i, K, draft)
+            else:
+                pf, ptau = pending[0]
+                dfl.dflash_step(ctx, pf, ptau, i, K, draft)
+            dfl.dflash_accept(draft, tg, wl.batch, K, acc)
+            pending[0] = (f, tau)
+
+        def flush():
+            if pending[0] is not None:
+                dfl.dflash_project_ctx(ctx, pending[0][0], pending[0][1])
+                pending[0] = None
+
+        # The same step as three calls: draft, accept, project.
+        def unfused(t):
             i, tg, tau, f = dev[t]
             dfl.dflash_draft_block(ctx, i, K, draft)
             dfl.dflash_accept(draft, tg, wl.batch, K, acc)
             dfl.dflash_project_ctx(ctx, f, tau)
 
         for t in range(args.warmup):
-            one(t)
+            fused(t)
         torch.cuda.synchronize()
         lens_start, _ = ctx.query()
         ctx.profile("lm_head")
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(args.warmup, args.warmup + args.steps):
-            one(t)
+            fused(t)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         prof = ctx.profile_read()
@@ -266,6 +290,15 @@ def main():
         lens_end, caps = ctx.query()
         ms_step = wall * 1e3 / args.steps
         toks = wl.batch * K / (wall / args.steps)
+
+        flush()
+        t1 = args.warmup + args.steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(t1, t1 + args.steps):
+            unfused(t)
+        torch.cuda.synchronize()
+        ms_unfused = (time.perf_counter() - t0) * 1e3 / args.steps
 
         lm_ms, lm_n = prof.get("lm_head", (0.0, 0))
         s = wl.shape
@@ -275,14 +308,17 @@ def main():
         achieved = lm_bytes / (lm_avg * 1e-3) / 1e9
         mean_ctx = [(a + b) / 2 for a, b in zip(lens_start, lens_end)]
         byt = block_bytes(s, mb, mean_ctx, K, wl.batch)
-        # per-phase times of a separate pass (every launch timed), outside the
-        # timed region so that the event records do not slow the step loop
+        # per-phase times of a separate pass of fused steps (every launch
+        # timed), outside the timed regions so that the event records do not
+        # slow the step loop
         n_ph = max(1, min(args.warmup, 10))
+        t2 = t1 + args.steps
         ctx.profile(True)
-        for t in range(n_ph):
-            one(t)
+        for t in range(t2, t2 + n_ph):
+            fused(t)
         allp = ctx.profile_read()
         ctx.profile(False)
+        flush()
         phases = {k: round(v[0] / n_ph, 4) for k, v in allp.items()}
         out = {
             "metric": METRIC,
@@ -300,6 +336,7 @@ def main():
             "config": {"workload": wl.name, "batch": wl.batch, "K": K, "ctx0": list(wl.ctx0)[:4],
                        "hidden": s.hidden, "layers": s.n_layers, "vocab": s.vocab,
                        "parallelism": "1 GPU"},
+            "unfused_ms_per_step": round(ms_unfused, 4),
             "draft_block_ms": round(draft_ms, 4),
             "draft_block_hbm_frac": round(block_bytes(s, mb, lens0, K, wl.batch) / (draft_ms * 1e-3) / 1e9
                                           / HBM_PEAK_GBS, 4),

@@ -64,7 +64,8 @@ class _Allocator(ctypes.Structure):
 
 EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_model_create",
            "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
-           "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_accept",
+           "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_step",
+           "dflash_accept",
            "dflash_ctx_query", "dflash_ctx_buffers", "dflash_profile_enable",
            "dflash_profile_read", "dflash_phase_name")
 NUM_PHASES = 15
@@ -90,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "dflash_ctx_destroy": ([vp], ctypes.c_int),
         "dflash_project_ctx": ([vp, vp, i32p, vp, vp], ctypes.c_int),
         "dflash_draft_block": ([vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
+        "dflash_step": ([vp, vp, ctypes.POINTER(ctypes.c_int32), vp, i32, vp, vp, vp, vp], ctypes.c_int),
         "dflash_accept": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
         "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
         "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
@@ -314,6 +316,23 @@ def dflash_draft_block(ctx: Context, block_ids: torch.Tensor, K: int, draft_ids:
     _check("dflash_draft_block",
            lib.dflash_draft_block(ctx.handle, _ptr(block_ids), int(K), _ptr(draft_ids),
                                   _ptr(logits), _ptr(hidden), _stream(stream)))
+
+
+def dflash_step(ctx: Context, feats: Optional[torch.Tensor], n_new: Sequence[int], block_ids: torch.Tensor,
+                K: int, draft_ids: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                hidden: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """dflash_project_ctx(feats, n_new) then dflash_draft_block(...), fused."""
+    nn = (ctypes.c_int32 * ctx.batch)(*[int(n) for n in n_new])
+    for t, dt in ((block_ids, torch.int32), (draft_ids, torch.int32)):
+        if t.dtype != dt or t.numel() != ctx.batch * K:
+            raise ValueError("block_ids / draft_ids must be int32 [batch, K]")
+    if logits is not None and (logits.dtype != torch.float32 or
+                               logits.numel() != ctx.batch * K * ctx.model.shape.vocab):
+        raise ValueError("logits must be float32 [batch, K, vocab]")
+    _check("dflash_step",
+           lib.dflash_step(ctx.handle, _ptr(feats) if feats is not None and feats.numel() else None, nn,
+                           _ptr(block_ids), int(K), _ptr(draft_ids), _ptr(logits), _ptr(hidden),
+                           _stream(stream)))
 
 
 def dflash_accept(draft_ids: torch.Tensor, target_ids: torch.Tensor, batch: int, K: int,

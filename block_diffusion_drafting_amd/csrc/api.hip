@@ -504,8 +504,9 @@ static EpiArgs base_epi(const dflash_ctx* c, int M) {
 template <typename T>
 static dflash_status run_gemm(dflash_ctx* c, int phase, int epi, const Packed& W, const Frag& X,
                               const void* Xrow, int ldx, int M, EpiArgs e, hipStream_t s,
-                              GemmPlan* plan_out = nullptr) {
+                              GemmPlan* plan_out = nullptr, bool force_split = false) {
   GemmPlan p = plan_gemm(epi, W, M, sizeof(T) == 2, Xrow != nullptr);
+  if (force_split && sizeof(T) == 2) p.split = true;
   dflash_status st;
   if (p.part_floats && (st = ensure(c->alloc, c->part, p.part_floats * sizeof(float)))) return st;
   GemmArgs g{};
@@ -525,15 +526,13 @@ static dflash_status run_gemm(dflash_ctx* c, int phase, int epi, const Packed& W
   return DFLASH_OK;
 }
 
+// (a2) growth: a sequence whose append would overflow its capacity gets
+// buffers of the next power of two of the new length, the held rows copied
+// (host-authoritative; enqueued before anything reads the buffers).
 template <typename T>
-static dflash_status project_impl(dflash_ctx* c, const void* feats, const int32_t* n_new,
-                                  const int32_t* positions, hipStream_t s) {
+static dflash_status grow_for(dflash_ctx* c, const int32_t* n_new, hipStream_t s) {
   const dflash_model* m = c->m;
   const int B = c->B, H = m->cfg.hidden;
-  std::vector<int32_t> start(B + 1, 0);
-  for (int b = 0; b < B; ++b) start[b + 1] = start[b] + n_new[b];
-  const int total = start[B];
-  // growth (host-authoritative; enqueued before anything reads the buffers)
   for (int b = 0; b < B; ++b) {
     DevSeq& v = c->seq[b];
     const int64_t need = (int64_t)v.ctx_len + n_new[b];
@@ -554,19 +553,35 @@ static dflash_status project_impl(dflash_ctx* c, const void* feats, const int32_
     c->alloc.put(v.vt);
     v = nv;
   }
-  if (total == 0) return DFLASH_OK;
+  return DFLASH_OK;
+}
+
+// Row starts of an append and the host context lengths before it.
+static RowInfo row_info(const dflash_ctx* c, const int32_t* n_new) {
+  RowInfo ri;
+  ri.start[0] = 0;
+  for (int b = 0; b < c->B; ++b) {
+    ri.start[b + 1] = ri.start[b] + n_new[b];
+    ri.ctx0[b] = c->seq[b].ctx_len;
+  }
+  return ri;
+}
+
+template <typename T>
+static dflash_status project_impl(dflash_ctx* c, const void* feats, const int32_t* n_new,
+                                  const int32_t* positions, hipStream_t s) {
+  const dflash_model* m = c->m;
+  const int B = c->B, H = m->cfg.hidden;
   dflash_status st;
+  if ((st = grow_for<T>(c, n_new, s))) return st;
+  const RowInfo ri = row_info(c, n_new);
+  const int total = ri.start[B];
+  if (total == 0) return DFLASH_OK;
   const int mtiles = (total + 15) / 16;
   Frag cb;
   if ((st = ensure(c->alloc, c->rowmap, sizeof(RowMap) * total)) ||
       (st = ensure_frag(c, c->c_hi, c->c_lo, sizeof(T) == 2, mtiles, m->fc.n_tiles * 16 * m->es / 64, s, cb)))
     return st;
-  RowInfo ri;
-  for (int b = 0; b < B; ++b) {
-    ri.start[b] = start[b];
-    ri.ctx0[b] = c->seq[b].ctx_len;
-  }
-  ri.start[B] = start[B];
   EpiArgs e = base_epi(c, total);
   e.cbuf = cb;
   e.rowmap = (const RowMap*)c->rowmap.p;
@@ -578,7 +593,7 @@ static dflash_status project_impl(dflash_ctx* c, const void* feats, const int32_
     if ((st = run_gemm<T>(c, PH_FC, EPI_PART, m->fc, none, feats, m->cfg.n_feat * H, total, e, s, &p))) return st;
     PhaseTimer tm(c, PH_FCFIN, s);
     HIP_TRY(launch_fc_finalize<T>((const float*)c->part.p, p.nsplit, mtiles, total, H, ri, B, positions,
-                                  (RowMap*)c->rowmap.p, c->seq_dev, cb, s));
+                                  (RowMap*)c->rowmap.p, c->seq_dev, cb, 0, s));
   } else {
     {
       PhaseTimer tm(c, PH_ROWMAP, s);
@@ -614,9 +629,17 @@ dflash_status dflash_project_ctx(dflash_ctx* c, const void* feats, const int32_t
 
 }  // extern "C"
 
+// Context rows of a fused step: projected features in the QKV activation
+// matrix from m-tile mt0 on, row map in the context's row-map buffer.
+struct FusedCtx {
+  int n_ctx = 0;
+  int mt0 = 0;
+  Frag x{};
+};
+
 template <typename T>
 static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_t* draft, float* logits,
-                                void* hidden, hipStream_t s) {
+                                void* hidden, hipStream_t s, const FusedCtx& fused = FusedCtx{}) {
   using CT = typename CacheOf<T>::type;
   const dflash_model* m = c->m;
   const dflash_config& cf = m->cfg;
@@ -697,7 +720,20 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
 
   const Frag none{};
   for (int l = 0; l < L; ++l) {
-    if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], xg, nullptr, 0, M, e, s))) return st;
+    if (fused.n_ctx > 0) {
+      // block rows and the appended context rows in one product: the
+      // context rows' K/V land in layer l's caches before its attention
+      EpiArgs ef = e;
+      ef.ctx_mt0 = fused.mt0;
+      ef.n_ctx = fused.n_ctx;
+      ef.layer = l;
+      ef.rowmap = (const RowMap*)c->rowmap.p;
+      if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], fused.x, nullptr, 0, fused.mt0 * 16 + fused.n_ctx, ef,
+                            s, nullptr, true)))
+        return st;
+    } else if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], xg, nullptr, 0, M, e, s))) {
+      return st;
+    }
     a.layer = l;
     {
       PhaseTimer tm(c, PH_ATTN, s);
@@ -732,7 +768,70 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   return DFLASH_OK;
 }
 
+// NEXT step in one call: project and append the accepted positions, then
+// draft the next block with their K/V injected by each layer's QKV product
+// (whose W_k / W_v stream anyway), so no separate injection product runs.
+// Appends too large for one activation matrix take the two-call path.
+template <typename T>
+static dflash_status step_impl(dflash_ctx* c, const void* feats, const int32_t* n_new, const int32_t* ids, int K,
+                               int32_t* draft, float* logits, void* hidden, hipStream_t s) {
+  const dflash_model* m = c->m;
+  const int B = c->B, H = m->cfg.hidden;
+  const RowInfo ri0 = row_info(c, n_new);
+  const int total = ri0.start[B];
+  const int mtb = (B * K + 15) / 16, mtc = (total + 15) / 16;
+  dflash_status st;
+  if (total == 0) return draft_impl<T>(c, ids, K, draft, logits, hidden, s);
+  if (m->cfg.n_layers == 0 || mtb + mtc > 4) {
+    if ((st = project_impl<T>(c, feats, n_new, nullptr, s))) return st;
+    return draft_impl<T>(c, ids, K, draft, logits, hidden, s);
+  }
+  if ((st = grow_for<T>(c, n_new, s))) return st;
+  const RowInfo ri = row_info(c, n_new);
+  FusedCtx fused;
+  fused.n_ctx = total;
+  fused.mt0 = mtb;
+  // the activation matrix spans whole m-tile groups of the QKV product, so
+  // that every load batch is a full one (rows past the data are never stored)
+  const int mt_all = mtb + mtc <= 2 ? mtb + mtc : 4;
+  if ((st = ensure(c->alloc, c->rowmap, sizeof(RowMap) * total)) ||
+      (st = ensure_frag(c, c->xg_hi, c->xg_lo, sizeof(T) == 2, mt_all, H * m->es / 64, s, fused.x)))
+    return st;
+  EpiArgs e = base_epi(c, total);
+  const Frag none{};
+  GemmPlan p;
+  if ((st = run_gemm<T>(c, PH_FC, EPI_PART, m->fc, none, feats, m->cfg.n_feat * H, total, e, s, &p))) return st;
+  {
+    PhaseTimer tm(c, PH_FCFIN, s);
+    HIP_TRY(launch_fc_finalize<T>((const float*)c->part.p, p.nsplit, mtc, total, H, ri, B, nullptr,
+                                  (RowMap*)c->rowmap.p, c->seq_dev, fused.x, mtb * 16, s));
+  }
+  for (int b = 0; b < B; ++b) c->seq[b].ctx_len += n_new[b];
+  return draft_impl<T>(c, ids, K, draft, logits, hidden, s, fused);
+}
+
 extern "C" {
+
+dflash_status dflash_step(dflash_ctx* c, const void* feats, const int32_t* n_new, const int32_t* block_ids,
+                          int32_t K, int32_t* draft_ids, float* logits, void* hidden, void* stream) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!n_new) return fail(DFLASH_E_ARG, "n_new is NULL");
+  if (!block_ids || !draft_ids) return fail(DFLASH_E_ARG, "block_ids / draft_ids is NULL");
+  if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
+  int64_t total = 0;
+  for (int b = 0; b < c->B; ++b) {
+    if (n_new[b] < 0) return fail(DFLASH_E_ARG, "n_new[%d] = %d is negative", b, n_new[b]);
+    if ((int64_t)c->seq[b].ctx_len + n_new[b] > (1 << 30))
+      return fail(DFLASH_E_SHAPE, "sequence %d would exceed 2^30 positions", b);
+    total += n_new[b];
+  }
+  if (total > (1 << 30)) return fail(DFLASH_E_SHAPE, "too many rows in one call");
+  if (total > 0 && !feats) return fail(DFLASH_E_ARG, "feats is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  return c->m->cfg.dtype == DFLASH_BF16
+             ? step_impl<bf16_t>(c, feats, n_new, block_ids, K, draft_ids, logits, hidden, s)
+             : step_impl<float>(c, feats, n_new, block_ids, K, draft_ids, logits, hidden, s);
+}
 
 dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* block_ids, int32_t K, int32_t* draft_ids,
                                  float* logits, void* hidden, void* stream) {

@@ -59,6 +59,34 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Context K/V rows: nn = offset inside one layer's [K rows | V rows] block
+// (K rows in RoPE pair order), row map rm of the context row, values acc.
+template <typename CT>
+__device__ __forceinline__ void store_ctx_kv(const EpiArgs& e, int l, int nn, const RowMap& rm, f32x4 acc,
+                                             int g4) {
+  const int kvd = e.nkv * e.d;
+  const DevSeq sq = e.seqs[rm.b];
+  if (nn < kvd) {
+    const int head = nn / e.d, th = (nn % e.d) / 16;
+    const int p0 = th * 8 + g4 * 2;
+    float a1, a2, b1, b2;
+    rope_pair(acc[0], acc[1], rm.pos, e.inv_freq[p0], a1, a2);
+    rope_pair(acc[2], acc[3], rm.pos, e.inv_freq[p0 + 1], b1, b2);
+    auto dst = gp((CT*)sq.k + (((size_t)l * e.nkv + head) * sq.phys + rm.slot) * e.d);
+    const int h2 = e.d / 2;
+    dst[p0] = Elem<CT>::from_f(a1);
+    dst[p0 + 1] = Elem<CT>::from_f(b1);
+    dst[p0 + h2] = Elem<CT>::from_f(a2);
+    dst[p0 + 1 + h2] = Elem<CT>::from_f(b2);
+  } else {
+    const int v = nn - kvd;
+    const int head = v / e.d, f0 = v % e.d + g4 * 4;
+    auto dst = gp((CT*)sq.vt + (((size_t)l * e.nkv + head) * e.d + f0) * sq.phys + rm.slot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[(size_t)j * sq.phys] = Elem<CT>::from_f(acc[j]);
+  }
+}
+
 // One complete 16x16 output tile: acc[j] is output row n = tile*16 +
 // 4*(lane/16) + j of activation row m = mt*16 + lane%16.  Runs on one wave.
 template <typename T, int EPI>
@@ -71,6 +99,17 @@ __device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 a
     if (mt >= e.part_mtiles) return;   // m-tile past the rows of the call: no slot
     *gp((f32x4*)(e.part + ((((size_t)s * e.part_ntiles + tile) * e.part_mtiles + mt) * 64 + lane) * 4)) = acc;
     return;
+  }
+  if constexpr (EPI == EPI_QKV) {
+    // context rows appended below the block (fused step): their K and V
+    // (no norm, no gain) go to this layer's caches; their Q is not needed
+    if (e.n_ctx > 0 && mt >= e.ctx_mt0) {
+      const int j = (mt - e.ctx_mt0) * 16 + (lane & 15);
+      const int qd = e.nq * e.d;
+      const int n = tile * 16;
+      if (j < e.n_ctx && n >= qd) store_ctx_kv<CT>(e, e.layer, n - qd, e.rowmap[j], acc, g4);
+      return;
+    }
   }
   if (m >= e.M) return;
   if constexpr (EPI == EPI_QKV) {
@@ -138,31 +177,9 @@ __device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 a
     float v[4] = {acc[0], acc[1], acc[2], acc[3]};
     frag_store<T, 4>(e.cbuf, m, n, v);
   } else if constexpr (EPI == EPI_KV) {
-    const int kvd = e.nkv * e.d;
     const int n = tile * 16;
-    const int l = n / (2 * kvd);
-    const int nn = n - l * 2 * kvd;
-    const RowMap rm = e.rowmap[m];
-    const DevSeq sq = e.seqs[rm.b];
-    if (nn < kvd) {
-      const int head = nn / e.d, th = (nn % e.d) / 16;
-      const int p0 = th * 8 + g4 * 2;
-      float a1, a2, b1, b2;
-      rope_pair(acc[0], acc[1], rm.pos, e.inv_freq[p0], a1, a2);
-      rope_pair(acc[2], acc[3], rm.pos, e.inv_freq[p0 + 1], b1, b2);
-      auto dst = gp((CT*)sq.k + (((size_t)l * e.nkv + head) * sq.phys + rm.slot) * e.d);
-      const int h2 = e.d / 2;
-      dst[p0] = Elem<CT>::from_f(a1);
-      dst[p0 + 1] = Elem<CT>::from_f(b1);
-      dst[p0 + h2] = Elem<CT>::from_f(a2);
-      dst[p0 + 1 + h2] = Elem<CT>::from_f(b2);
-    } else {
-      const int v = nn - kvd;
-      const int head = v / e.d, f0 = v % e.d + g4 * 4;
-      auto dst = gp((CT*)sq.vt + (((size_t)l * e.nkv + head) * e.d + f0) * sq.phys + rm.slot);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(size_t)j * sq.phys] = Elem<CT>::from_f(acc[j]);
-    }
+    const int l = n / (2 * e.nkv * e.d);
+    store_ctx_kv<CT>(e, l, n - l * 2 * e.nkv * e.d, e.rowmap[m], acc, g4);
   }
 }
 
@@ -405,25 +422,28 @@ inline hipError_t launch_v(const GemmPlan& p, const GemmArgs& g, const EpiArgs& 
 
 template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT>
 inline hipError_t launch_h(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  // one m-tile: eight waves stream; two or four m-tiles: four waves (one
-  // per SIMD, large accumulator sets) with the next load batch in flight
-  // during the MFMAs of the current one
-  // (two batches in registers: half the batch size).  Eight m-tiles: eight
-  // waves of single batches measured faster than four pipelined waves.
-  constexpr int WAVES = MTT == 1 || MTT == 8 ? 8 : 4;
-  constexpr bool PIPE = MTT == 2 || MTT == 4;
+  // Measured on the Qwen3-4B shapes: eight waves for one, two and eight
+  // m-tiles; the pipelined form (the next load batch in flight during the
+  // MFMAs of the current one; two batches in registers, so half the batch
+  // size) for four m-tiles and for two m-tiles over at most two tiles per
+  // workgroup.
+  constexpr int WAVES = MTT == 4 ? 4 : 8;
+  constexpr bool PIPE = MTT == 4 || (MTT == 2 && NTG <= 2);
   constexpr int CHK = MTT > 1 ? (HotChk<MTT, NTG, SPLIT>::value + 1) / 2 : HotChk<MTT, NTG, SPLIT>::value;
   return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>(p, g, e, s);
 }
 
 // Compiled combinations: bf16 draft products use the hi/lo activation pair
-// exactly when a workgroup holds at most two m-tiles; the per-step context
+// when a workgroup holds at most two m-tiles; the per-step context
 // products (row-major features, K/V injection) have at most two m-tiles,
 // and K/V injection always uses the pair for bf16.
 template <typename T, int MTT, int EPI, bool ROW, bool SPLIT>
 constexpr bool compiled() {
   if constexpr (ROW) return !SPLIT && MTT <= 2;
   if constexpr (EPI == EPI_KV) return MTT <= 2 && SPLIT == (sizeof(T) == 2);
+  // QKV of a fused step (block + context rows, up to four m-tiles) keeps
+  // the pair for the injected context K/V
+  if constexpr (EPI == EPI_QKV && sizeof(T) == 2 && MTT == 4) return true;
   return sizeof(T) == 4 ? !SPLIT : (SPLIT == (MTT <= 2));
 }
 

@@ -69,7 +69,10 @@ struct EpiArgs {
   float* logits;            // [M][V] or null
   unsigned long long* keys; // [M] argmax keys
   Frag cbuf;                // context features, frag layout over hidden
-  const RowMap* rowmap;     // [M]
+  const RowMap* rowmap;     // [M] (EPI_FC, EPI_KV) or [n_ctx] (fused QKV)
+  // fused step: context rows appended to the QKV activations from m-tile
+  // ctx_mt0 on; their K/V go to layer `layer` of the caches
+  int32_t ctx_mt0, n_ctx, layer;
 };
 
 struct GemmArgs {
@@ -136,12 +139,13 @@ struct RowInfo {
   int32_t start[DFLASH_ROWMAP_MAX + 1];
   int32_t ctx0[DFLASH_ROWMAP_MAX];
 };
-// c = sum of split-K partials -> context buffer rows + staging frag; also
-// writes the row map and advances the device context lengths.
+// c = sum of split-K partials -> context buffer rows + staging frag (rows
+// from row0 on); also writes the row map and advances the device context
+// lengths.
 template <typename T>
 hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri, int B,
                               const int32_t* positions, RowMap* rowmap, DevSeq* seqs, Frag cbuf,
-                              hipStream_t s);
+                              int row0, hipStream_t s);
 // draft ids from argmax keys; optional final-normed hidden rows.
 template <typename T>
 hipError_t launch_finalize(const unsigned long long* keys, int M, int32_t* draft, const float* x,

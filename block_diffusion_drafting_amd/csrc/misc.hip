@@ -148,7 +148,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void fc_finalize_kernel(const float* part, int nsplit, int mtiles,
                                                           int M, int H, RowInfo ri, int B,
                                                           const int32_t* positions, RowMap* rowmap,
-                                                          DevSeq* seqs, Frag cbuf) {
+                                                          DevSeq* seqs, Frag cbuf, int row0) {
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int b = threadIdx.x; b < B; b += blockDim.x) seqs[b].ctx_len = ri.ctx0[b] + ri.start[b + 1] - ri.start[b];
   const int m = blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -159,23 +159,23 @@ __global__ __launch_bounds__(256) void fc_finalize_kernel(const float* part, int
   const f32x4 c = sum_parts(part, nsplit, H / 16, mtiles, m, n0);
   *gp((f32x4*)((float*)seqs[rm.b].ctxbuf + (size_t)rm.slot * H + n0)) = c;
   float v[4] = {c[0], c[1], c[2], c[3]};
-  frag_store<T, 4>(cbuf, m, n0, v);
+  frag_store<T, 4>(cbuf, row0 + m, n0, v);
 }
 
 template <typename T>
 hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri, int B,
                               const int32_t* positions, RowMap* rowmap, DevSeq* seqs, Frag cbuf,
-                              hipStream_t s) {
+                              int row0, hipStream_t s) {
   if (B > DFLASH_ROWMAP_MAX) return hipErrorInvalidValue;
   dim3 grid((M + 15) / 16, H / 64);
   hipLaunchKernelGGL((fc_finalize_kernel<T>), grid, dim3(256), 0, s, part, nsplit, mtiles, M, H, ri, B,
-                     positions, rowmap, seqs, cbuf);
+                     positions, rowmap, seqs, cbuf, row0);
   return hipGetLastError();
 }
 template hipError_t launch_fc_finalize<bf16_t>(const float*, int, int, int, int, const RowInfo&, int,
-                                               const int32_t*, RowMap*, DevSeq*, Frag, hipStream_t);
+                                               const int32_t*, RowMap*, DevSeq*, Frag, int, hipStream_t);
 template hipError_t launch_fc_finalize<float>(const float*, int, int, int, int, const RowInfo&, int,
-                                              const int32_t*, RowMap*, DevSeq*, Frag, hipStream_t);
+                                              const int32_t*, RowMap*, DevSeq*, Frag, int, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // (a9) end of the block: draft ids from the argmax keys; optionally the

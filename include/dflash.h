@@ -184,6 +184,21 @@ dflash_status dflash_draft_block(dflash_ctx *c, const int32_t *block_ids, int32_
                                  int32_t *draft_ids, float *logits, void *hidden,
                                  void *stream);
 
+/* (a1)-(a9) in one call: dflash_project_ctx(feats, n_new, positions = NULL)
+ * followed by dflash_draft_block(block_ids, K, ...), with the same results
+ * up to rounding.  The projected features of the appended positions join
+ * the block rows in each layer's Q/K/V product, which writes their K and V
+ * into that layer's cache (the W_k / W_v of the layer stream once for both;
+ * kongchang.com, "Innovation 2: target-feature KV injection"; Google
+ * Developers Blog, "Smart context management": only newly accepted
+ * positions are projected).  Appends of more than 64 rows in all, or whose
+ * rows and the block's need more than four 16-row tiles, run as the two
+ * separate calls.  Arguments, ownership and errors as in those calls;
+ * state advances by n_new exactly as dflash_project_ctx does. */
+dflash_status dflash_step(dflash_ctx *c, const void *feats, const int32_t *n_new,
+                          const int32_t *block_ids, int32_t K, int32_t *draft_ids,
+                          float *logits, void *hidden, void *stream);
+
 /* (a10): greedy acceptance (Google Developers Blog, "Overcoming the
  * autoregressive bottleneck"; table 2 caption: greedy decoding).
  *   draft_ids, target_ids dev [batch, K] int32; accept_len dev [batch] int32

@@ -143,6 +143,28 @@ class Pair:
             out["hidden"] = O.to_f64(h, s.dtype)
         return out
 
+    def gpu_step(self, feats_per_seq, ids, logits=True, hidden=True):
+        """dflash_step: append feats_per_seq[b] to sequence b and draft ids
+        (the oracle states are advanced by the caller)."""
+        B, K = ids.shape
+        s = self.shape
+        n_new = [len(f) for f in feats_per_seq]
+        nonempty = [f for f in feats_per_seq if len(f)]
+        fd = to_dev(np.concatenate(nonempty, axis=0)) if nonempty else None
+        idd = to_dev(ids.astype(np.int32))
+        dr = torch.empty(B, K, dtype=torch.int32, device="cuda")
+        lg = torch.empty(B, K, s.vocab, dtype=torch.float32, device="cuda") if logits else None
+        hd = (torch.empty(B, K, s.hidden, dtype=torch.uint16 if s.dtype == "bf16" else torch.float32,
+                          device="cuda") if hidden else None)
+        self.dfl.dflash_step(self.ctx, fd, n_new, idd, K, dr, lg, hd)
+        torch.cuda.synchronize()
+        out = {"draft": dr.cpu().numpy()}
+        if logits:
+            out["logits"] = lg.cpu().numpy()
+        if hidden:
+            out["hidden"] = O.to_f64(hd.cpu().numpy(), s.dtype)
+        return out
+
     def oracle_draft(self, b, ids_b):
         return O.draft_one(self.om, self.ost[b], ids_b)
 

@@ -193,9 +193,13 @@ def test_accept_kernel_exhaustive_patterns():
         assert np.array_equal(out.cpu().numpy(), O.accept(d, t))
 
 
-def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=()):
+def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=(), fused=False):
     """GPU session and oracle session in lockstep; tau, ctx_len and cap must
-    be identical every step; outputs compared on the checked steps."""
+    be identical every step; outputs compared on the checked steps.  With
+    `fused`, the accepted positions of step t are appended by the
+    dflash_step call that drafts step t + 1 (and by a final
+    dflash_project_ctx), so the GPU state lags the oracle's by one append
+    between calls."""
     import block_diffusion_drafting_amd as dfl
     seqs = list(range(wl.batch)) if batch_seqs is None else batch_seqs
     w = _weights(shape, wl.seed)
@@ -208,11 +212,20 @@ def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=()):
     anchors = [synth.first_anchor(wl.seed, b, shape.vocab) for b in range(wl.batch)]
     p.check_state()
     K = wl.K
+    pending = None          # (features per sequence, taus) not yet appended on the GPU
+    prev = None             # previous oracle step record
     for t in range(steps):
         ids = np.stack([synth.block_ids(wl.seed, b, t, K, shape.vocab) for b in range(wl.batch)])
         ids[:, 0] = anchors
         check = (t % check_every == 0) or (t in tail_check) or t == steps - 1
-        g = p.gpu_draft(ids, logits=check, hidden=False)
+        if pending is not None:
+            g = p.gpu_step(pending, ids, logits=check, hidden=False)
+            lens, caps = p.ctx.query()
+            assert [lens[b] for b in seqs] == prev.ctx_len.tolist()
+            assert [caps[b] for b in seqs] == prev.cap.tolist()
+            pending = None
+        else:
+            g = p.gpu_draft(ids, logits=check, hidden=False)
         draws = [synth.verifier_draws(wl.seed, b, t, K, shape.vocab, wl.a[b], wl.gamma) for b in range(wl.batch)]
         target = np.stack([synth.target_tokens(g["draft"][b], draws[b], shape.vocab) for b in range(wl.batch)])
         tau_d = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
@@ -227,13 +240,19 @@ def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=()):
                 check_argmax(g["draft"][b], rec.logits[i])
         # commit tau positions on the GPU side (oracle did it inside step)
         fe = [synth.step_features(shape, wl.seed, b, t, int(tau[b])) for b in range(wl.batch)]
-        p.dfl.dflash_project_ctx(p.ctx, to_dev(np.concatenate(fe, axis=0)), [int(x) for x in tau])
         anchors = [draws[b].bonus for b in range(wl.batch)]
+        assert osess.violations() == []
+        if fused:
+            pending, prev = fe, rec
+            say(f"  step {t}: tau={tau.tolist()[:4]} (appended by the next step)")
+            continue
+        p.dfl.dflash_project_ctx(p.ctx, to_dev(np.concatenate(fe, axis=0)), [int(x) for x in tau])
         lens, caps = p.ctx.query()
         assert [lens[b] for b in seqs] == rec.ctx_len.tolist()
         assert [caps[b] for b in seqs] == rec.cap.tolist()
-        assert osess.violations() == []
         say(f"  step {t}: tau={tau.tolist()[:4]} ctx={lens[:4]} cap={caps[:4]}")
+    if pending is not None:
+        p.dfl.dflash_project_ctx(p.ctx, to_dev(np.concatenate(pending, axis=0)), [len(f) for f in pending])
     p.check_state()
     return p
 
@@ -249,6 +268,72 @@ def test_session_small_bf16_growth():
     say("case: session small bf16 with growth")
     wl = synth.workload(2).replace(shape=SMALL, ctx0=(60, 5), batch=2, a=(0.9, 0.7), K=10)
     _session(SMALL, wl, 12)
+
+
+def test_fused_step_matches_oracle():
+    """dflash_step (append + draft in one call, context K/V written by the
+    QKV products) against the oracle's project + draft: logits, final hidden
+    states, context buffer and caches; two sequences with 5 and 11 new rows,
+    then one with none."""
+    say("case: fused step small bf16")
+    p = Pair(SMALL, 41, 2, gain_std=0.1)
+    _prefill(p, [70, 33], seed=41)
+    for t, n_new in enumerate([(5, 11), (0, 3), (17, 0)]):
+        feats = [synth.step_features(SMALL, 41, b, t, n) for b, n in enumerate(n_new)]
+        ids = _ids(41 + t, 2, 16, SMALL.vocab)
+        g = p.gpu_step(feats, ids)
+        for b in range(2):
+            if n_new[b]:
+                O.project_ctx(p.om, p.ost[b], feats[b])
+            d_o, l_o, z_o = p.oracle_draft(b, ids[b])
+            check_rows(f"t{t} logits[{b}]", g["logits"][b], l_o, tol(SMALL))
+            check_rows(f"t{t} hidden[{b}]", g["hidden"][b], z_o, tol(SMALL))
+            check_argmax(g["draft"][b], l_o)
+        p.check_state()
+
+
+def test_fused_step_fp32_and_large_append():
+    """Tiny fp32 model: a fused step (8 rows) and one whose append is too
+    large to fuse (two-call path inside dflash_step), both against the
+    oracle."""
+    say("case: fused step tiny fp32")
+    wl = synth.workload(0)
+    s = wl.shape
+    p = Pair(s, 43, 1, gain_std=0.1)
+    _prefill(p, [40], seed=43)
+    for t, n in enumerate([8, 70]):
+        feats = [synth.step_features(s, 43, 0, t, n)]
+        ids = _ids(43 + t, 1, 8, s.vocab)
+        g = p.gpu_step(feats, ids)
+        O.project_ctx(p.om, p.ost[0], feats[0])
+        d_o, l_o, z_o = p.oracle_draft(0, ids[0])
+        check_rows(f"t{t} logits", g["logits"][0], l_o, tol(s))
+        check_rows(f"t{t} hidden", g["hidden"][0], z_o, tol(s))
+        check_argmax(g["draft"][0], l_o)
+        p.check_state()
+
+
+def test_fused_session_small_bf16_growth():
+    say("case: fused session small bf16 with growth")
+    wl = synth.workload(2).replace(shape=SMALL, ctx0=(60, 5), batch=2, a=(0.9, 0.7), K=10)
+    _session(SMALL, wl, 12, fused=True)
+
+
+@pytest.mark.slow
+def test_fused_session_workload1_qwen3_4b_shape():
+    """Workload 1 session through dflash_step (16 steps, logits at 0, 7, 15)."""
+    say("case: fused session workload 1")
+    wl = synth.workload(1)
+    _session(wl.shape, wl, wl.steps, check_every=8, fused=True)
+
+
+@pytest.mark.slow
+def test_fused_session_workload2_llama_growth():
+    """Workload 2 session through dflash_step: 64 steps with the first
+    append growing the buffers from 4096 to 8192 rows."""
+    say("case: fused session workload 2")
+    wl = synth.workload(2)
+    _session(wl.shape, wl, wl.steps, check_every=32, tail_check=(1,), fused=True)
 
 
 @pytest.mark.slow
