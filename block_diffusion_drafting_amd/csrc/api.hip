@@ -650,7 +650,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   const bool pair = sizeof(T) == 2;
   dflash_status st;
   Frag xg, of, af;
-  if ((st = ensure(c->alloc, c->x, (size_t)M * H * 4)) || (st = ensure(c->alloc, c->ssq, (size_t)G * M * 4)) ||
+  if ((st = ensure(c->alloc, c->x, (size_t)M * H * 4)) || (st = ensure(c->alloc, c->ssq, (size_t)(H / 16) * M * 4)) ||
       (st = ensure(c->alloc, c->q, (size_t)M * nq * d * ces)) ||
       (st = ensure(c->alloc, c->bk, (size_t)B * nkv * Kpad * d * ces)) ||
       (st = ensure(c->alloc, c->bvt, (size_t)B * nkv * Kpad * d * ces)) ||
@@ -744,13 +744,26 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
       HIP_TRY((launch_attn_combine<CT, T>(a, of, s)));
     }
     GemmPlan p;
-    if ((st = run_gemm<T>(c, PH_O, EPI_PART, m->o[l], of, nullptr, 0, M, e, s, &p))) return st;
-    {
+    EpiArgs eg = e;
+    if (mtiles == 1) {
+      // one m-tile: the output projection runs over the whole reduction and
+      // its epilogue adds into the residual and writes the MLP norm's
+      // inputs (sums of squares per 16 columns), so no residual pass runs
+      // (with more rows the split form is faster)
+      EpiArgs eo = e;
+      eo.xres = (float*)c->x.p;
+      eo.gain = m->mlp_gain(l);
+      eo.xout = xg;
+      eo.ssq_out = (float*)c->ssq.p;
+      if ((st = run_gemm<T>(c, PH_O, EPI_RESNORM, m->o[l], of, nullptr, 0, M, eo, s))) return st;
+      eg.ssq_groups = H / 16;
+    } else {
+      if ((st = run_gemm<T>(c, PH_O, EPI_PART, m->o[l], of, nullptr, 0, M, e, s, &p))) return st;
       PhaseTimer tm(c, PH_RESID, s);
       HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
                                    m->mlp_gain(l), xg, (float*)c->ssq.p, s));
     }
-    if ((st = run_gemm<T>(c, PH_GU, EPI_SWIGLU, m->gu[l], xg, nullptr, 0, M, e, s))) return st;
+    if ((st = run_gemm<T>(c, PH_GU, EPI_SWIGLU, m->gu[l], xg, nullptr, 0, M, eg, s))) return st;
     if ((st = run_gemm<T>(c, PH_DOWN, EPI_PART, m->down[l], af, nullptr, 0, M, e, s, &p))) return st;
     {
       PhaseTimer tm(c, PH_RESID, s);

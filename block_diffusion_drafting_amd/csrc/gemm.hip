@@ -85,6 +85,7 @@ hipError_t launch_gemm(int epi, const GemmPlan& p, const GemmArgs& g, const EpiA
     case EPI_ARGMAX: return launch_gemm_epi<T, EPI_ARGMAX>(p, g, e, s);
     case EPI_FC: return launch_gemm_epi<T, EPI_FC>(p, g, e, s);
     case EPI_KV: return launch_gemm_epi<T, EPI_KV>(p, g, e, s);
+    case EPI_RESNORM: return launch_gemm_epi<T, EPI_RESNORM>(p, g, e, s);
   }
   return hipErrorInvalidValue;
 }

@@ -25,20 +25,6 @@ namespace dflash {
 // ---------------------------------------------------------------------------
 // epilogue helpers
 // ---------------------------------------------------------------------------
-// RMSNorm scale of row m from the per-column-group sums of squares; the
-// loads are independent so they are issued together.
-__device__ __forceinline__ float norm_scale(const EpiArgs& e, int m) {
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int g = 0;
-  for (; g + 8 <= e.ssq_groups; g += 8) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += e.ssq[(size_t)(g + i) * e.M + m];
-  }
-  for (; g < e.ssq_groups; ++g) acc[0] += e.ssq[(size_t)g * e.M + m];
-  const float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-  return rsqrtf(s / (float)e.norm_dim + e.eps);
-}
-
 constexpr bool needs_norm(int epi) { return epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_ARGMAX; }
 
 __device__ __forceinline__ void rope_pair(float x1, float x2, int pos, double inv, float& o1,
@@ -95,6 +81,30 @@ __device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 a
   using CT = typename CacheOf<T>::type;
   const int g4 = lane >> 4;
   const int m = mt * 16 + (lane & 15);
+  if constexpr (EPI == EPI_RESNORM) {
+    // x[m][n..n+3] += y; x * gain -> frag; sum of squares of the tile's 16
+    // columns of row m (all lanes take part in the reduction)
+    const int n = tile * 16 + g4 * 4;
+    const bool ok = m < e.M;
+    float ss = 0.f;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      auto xp = gp((f32x4*)(e.xres + (size_t)m * e.H + n));
+      f32x4 x = *xp + acc;
+      *xp = x;
+      const f32x4 gn = gld((const f32x4*)(e.gain + n));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ss = fmaf(x[j], x[j], ss);
+        v[j] = x[j] * gn[j];
+      }
+      frag_store<T, 4>(e.xout, m, n, v);
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (ok && g4 == 0) e.ssq_out[(size_t)tile * e.M + m] = ss;
+    return;
+  }
   if constexpr (EPI == EPI_PART) {
     if (mt >= e.part_mtiles) return;   // m-tile past the rows of the call: no slot
     *gp((f32x4*)(e.part + ((((size_t)s * e.part_ntiles + tile) * e.part_mtiles + mt) * 64 + lane) * 4)) = acc;
@@ -262,11 +272,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
   for (int t = 0; t < NTG; ++t)
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the norm scale of this workgroup's rows, loaded while the weights stream
+  // the norm scale of this workgroup's rows, loaded while the weights
+  // stream: thread (part p, row r) adds groups p, p + P, ... of row r; the
+  // P parts are then added in order
   if constexpr (needs_norm(EPI)) {
-    if (threadIdx.x < MTT * 16) {
-      const int m = mt0 * 16 + threadIdx.x;
-      rnorm[threadIdx.x] = m < e.M ? norm_scale(e, m) : 0.f;
+    constexpr int R = MTT * 16, P = WAVES * 64 / R;
+    __shared__ float npart[P][R];
+    const int r = threadIdx.x % R, part = threadIdx.x / R;
+    const int m = mt0 * 16 + r;
+    float sum = 0.f;
+    if (m < e.M) {
+#pragma unroll 4
+      for (int g = part; g < e.ssq_groups; g += P) sum += e.ssq[(size_t)g * e.M + m];
+    }
+    npart[part][r] = sum;
+    __syncthreads();
+    if (threadIdx.x < R) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < P; ++q) t += npart[q][threadIdx.x];
+      rnorm[threadIdx.x] = m < e.M ? rsqrtf(t / (float)e.norm_dim + e.eps) : 0.f;
     }
   }
 

@@ -1,7 +1,10 @@
-// Compiled variants of the weight-streaming product with the EPI_PART epilogue.
+// Compiled variants of the output-side products: EPI_PART (split-K partial
+// tiles) and EPI_RESNORM (full-K, residual add and the next norm's inputs).
 #include "gemm_kernel.h"
 
 namespace dflash {
 template hipError_t launch_gemm_epi<bf16_t, EPI_PART>(const GemmPlan&, GemmArgs, const EpiArgs&, hipStream_t);
 template hipError_t launch_gemm_epi<float, EPI_PART>(const GemmPlan&, GemmArgs, const EpiArgs&, hipStream_t);
+template hipError_t launch_gemm_epi<bf16_t, EPI_RESNORM>(const GemmPlan&, GemmArgs, const EpiArgs&, hipStream_t);
+template hipError_t launch_gemm_epi<float, EPI_RESNORM>(const GemmPlan&, GemmArgs, const EpiArgs&, hipStream_t);
 }  // namespace dflash

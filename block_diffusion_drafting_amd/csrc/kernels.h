@@ -26,6 +26,9 @@ enum Epi : int {
   EPI_ARGMAX = 3,  // norm scale, optional logits, per-row argmax keys
   EPI_FC = 4,      // full context projection rows -> context buffer + staging
   EPI_KV = 5,      // K (RoPE) / V^T rows -> every layer's cache
+  EPI_RESNORM = 6, // full-K product added into the residual x; the next
+                   // RMSNorm's inputs (x * gain -> frag, sums of squares per
+                   // 16 columns) written alongside
 };
 
 // A weight matrix repacked into 16-row x 64-byte blocks (see common.h):
@@ -73,6 +76,12 @@ struct EpiArgs {
   // fused step: context rows appended to the QKV activations from m-tile
   // ctx_mt0 on; their K/V go to layer `layer` of the caches
   int32_t ctx_mt0, n_ctx, layer;
+  // EPI_RESNORM: residual x [M][H] (fp32), gain of the next norm, its frag
+  // output and sums of squares [H/16][M]
+  float* xres;
+  const float* gain;
+  Frag xout;
+  float* ssq_out;
 };
 
 struct GemmArgs {
