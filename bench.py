@@ -52,39 +52,48 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=25)
     ap.add_argument("--ksweep", action="store_true")
     ap.add_argument("--draft-iters", type=int, default=50)
+    ap.add_argument("--persistent", action="store_true",
+                    help="draft with the single-launch block where it applies (batch * K <= 16)")
+    ap.add_argument("--trace", action="store_true",
+                    help="report the single-launch block's per-phase timeline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_argmax_qwen3_4b_k16_traffic.txt")
-KERNEL_SOURCES = ["gemm_kernel.h", "gemm_argmax.hip", "gemm.hip", "kernels.h", "common.h"]
+# dominant kernel -> (counter summary, the sources its code comes from)
+TRAFFIC = {
+    "lm_head": ("lm_head_argmax_qwen3_4b_k16_traffic.txt",
+                ["gemm_kernel.h", "gemm_argmax.hip", "gemm.hip", "kernels.h", "common.h"]),
+    "persistent_draft": ("persistent_draft_qwen3_4b_k16_traffic.txt",
+                         ["persist.hip", "kernels.h", "common.h"]),
+}
 
 
-def kernel_source_hash():
-    """sha256 over the sources of the LM-head kernel (counter readings taken
-    from an older build are not reported)."""
+def kernel_source_hash(kernel: str):
+    """sha256 over the sources of a kernel (counter readings taken from an
+    older build are not reported)."""
     import hashlib
     h = hashlib.sha256()
-    for n in KERNEL_SOURCES:
+    for n in TRAFFIC[kernel][1]:
         with open(os.path.join(ROOT, "block_diffusion_drafting_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, K: int):
-    """HBM bytes per LM-head launch from the committed counter summary
+def measured_traffic(kernel: str, workload: str, K: int):
+    """HBM bytes per launch of `kernel` from its committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
     the summary is missing, was taken on another workload, or the kernel
     sources changed since."""
     try:
         vals = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", TRAFFIC[kernel][0])) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     vals[k.strip()] = v.strip()
-        if vals.get("source_sha256") != kernel_source_hash():
+        if vals.get("source_sha256") != kernel_source_hash(kernel):
             return None
         if vals.get("workload") != f"{workload} K={K}":
             return None
@@ -106,6 +115,39 @@ def copy_calibration(torch):
     del a, b
 
 
+def persist_timeline(tr, n_layers):
+    """Per-phase figures (us) from a single-launch block's timeline
+    [workgroups, 8 slots per phase] of 100 MHz ticks: for each phase (mean
+    over layers), the median and slowest workgroup's time from the phase
+    start to each mark inside it (1-5) and to its barrier arrival (6), and
+    the barrier's latency from the last arrival to the first release."""
+    names = ["embed"] + [n for _ in range(n_layers) for n in ("qkv", "attention", "o_proj", "gate_up", "down")]
+    names.append("lm_head")
+    tr = tr.astype(np.int64).reshape(tr.shape[0], -1, 8)
+    acc = {}
+    for p, name in enumerate(names):
+        ph = tr[:, p, :]
+        st = ph[:, 0]
+        d = acc.setdefault(name, {"n": 0})
+        d["n"] += 1
+        for k in range(1, 7):
+            ok = ph[:, k] > 0
+            if not ok.any():
+                continue
+            dt = (ph[ok, k] - st[ok]) / 100.0
+            key = "arrive" if k == 6 else f"m{k}"
+            d[key + "_med"] = d.get(key + "_med", 0.0) + float(np.median(dt))
+            d[key + "_max"] = d.get(key + "_max", 0.0) + float(dt.max())
+        if ph[:, 7].max() > 0:
+            d["barrier"] = d.get("barrier", 0.0) + (ph[:, 7].min() - ph[:, 6].max()) / 100.0
+    res = {}
+    for name, d in acc.items():
+        n = d.pop("n")
+        res[name] = {k: round(v / n, 2) for k, v in d.items()}
+    res["total_us"] = round((tr[:, -1, 6].max() - tr[:, 0, 0].min()) / 100.0, 2)
+    return res
+
+
 def setup(wl, K, dfl, torch):
     import synth
     t0 = time.time()
@@ -114,6 +156,8 @@ def setup(wl, K, dfl, torch):
     wd = dfl.weights_to_device(w)
     model = dfl.Model(wl.shape, wd)
     ctx = dfl.Context(model, wl.batch)
+    if getattr(setup, "persistent", False):
+        ctx.set_persistent(True)
     feats = [synth.prefill_features(wl.shape, wl.seed, b, wl.ctx0[b]) for b in range(wl.batch)]
     t0 = time.time()
     dfl.dflash_project_ctx(ctx, torch.from_numpy(np.concatenate(feats)).cuda(), list(wl.ctx0))
@@ -198,6 +242,7 @@ def main():
         copy_calibration(torch)
     wl = synth.workload(3 if args.ksweep else args.workload)
     Ks = list(wl.k_sweep) if args.ksweep else [args.K or wl.K]
+    setup.persistent = args.persistent
     w, wd, model, ctx = setup(wl, Ks[0], dfl, torch)
     mb = model.bytes()
     stream = torch.cuda.current_stream()
@@ -274,11 +319,15 @@ def main():
             dfl.dflash_accept(draft, tg, wl.batch, K, acc)
             dfl.dflash_project_ctx(ctx, f, tau)
 
+        # the dominant kernel: the whole block as one launch where the
+        # single-launch path applies, else the LM head product
+        persistent = ctx.persistent_path(K)
+        dom = "persistent_draft" if persistent else "lm_head"
         for t in range(args.warmup):
             fused(t)
         torch.cuda.synchronize()
         lens_start, _ = ctx.query()
-        ctx.profile("lm_head")
+        ctx.profile(dom)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(args.warmup, args.warmup + args.steps):
@@ -300,14 +349,19 @@ def main():
         torch.cuda.synchronize()
         ms_unfused = (time.perf_counter() - t0) * 1e3 / args.steps
 
-        lm_ms, lm_n = prof.get("lm_head", (0.0, 0))
+        dom_ms, dom_n = prof.get(dom, (0.0, 0))
         s = wl.shape
         M = wl.batch * K
-        lm_bytes = s.vocab * s.hidden * s.elem_bytes + M * s.hidden * s.elem_bytes + M * 4
-        lm_avg = lm_ms / max(lm_n, 1)
-        achieved = lm_bytes / (lm_avg * 1e-3) / 1e9
         mean_ctx = [(a + b) / 2 for a, b in zip(lens_start, lens_end)]
         byt = block_bytes(s, mb, mean_ctx, K, wl.batch)
+        if persistent:
+            dom_bytes = byt
+            dom_name = "persistent draft block (persist_draft_kernel: embed, 5 layers, LM head + argmax)"
+        else:
+            dom_bytes = s.vocab * s.hidden * s.elem_bytes + M * s.hidden * s.elem_bytes + M * 4
+            dom_name = "LM head product + argmax (gemm_kernel, EPI_ARGMAX)"
+        dom_avg = dom_ms / max(dom_n, 1)
+        achieved = dom_bytes / (dom_avg * 1e-3) / 1e9 if dom_avg > 0 else 0.0
         # per-phase times of a separate pass of fused steps (every launch
         # timed), outside the timed regions so that the event records do not
         # slow the step loop
@@ -320,6 +374,16 @@ def main():
         ctx.profile(False)
         flush()
         phases = {k: round(v[0] / n_ph, 4) for k, v in allp.items()}
+        timeline = None
+        if args.trace and persistent:
+            ctx.profile("persistent_draft")
+            for _ in range(3):
+                dfl.dflash_draft_block(ctx, dev[0][0], K, draft)
+            ctx.profile_read()
+            ctx.profile(False)
+            timeline = persist_timeline(ctx.persist_trace(), s.n_layers)
+            for k, v in timeline.items():
+                log(f"[bench] timeline {k}: {v}")
         out = {
             "metric": METRIC,
             "value": round(toks, 1),
@@ -342,11 +406,13 @@ def main():
                                           / HBM_PEAK_GBS, 4),
             "step_hbm_frac": round(byt / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "phase_ms_per_step": phases,
-            "roofline": {"kernel": "LM head product + argmax (gemm_kernel, EPI_ARGMAX)",
+            "draft_path": "single launch" if persistent else "per-product kernels",
+            "persist_timeline_us": timeline,
+            "roofline": {"kernel": dom_name,
                          "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(wl.name, K), "avg_launch_ms": round(lm_avg, 5),
-                         "bytes_per_launch": lm_bytes},
+                         "traffic": measured_traffic(dom, wl.name, K), "avg_launch_ms": round(dom_avg, 5),
+                         "launches": dom_n, "bytes_per_launch": int(dom_bytes)},
         }
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(wl, K, w, args.cpu_steps)

@@ -66,9 +66,11 @@ EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_
            "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
            "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_step",
            "dflash_accept",
-           "dflash_ctx_query", "dflash_ctx_buffers", "dflash_profile_enable",
+           "dflash_ctx_query", "dflash_ctx_buffers", "dflash_ctx_set_persistent",
+           "dflash_ctx_persistent_path", "dflash_ctx_check", "dflash_persist_trace",
+           "dflash_profile_enable",
            "dflash_profile_read", "dflash_phase_name")
-NUM_PHASES = 15
+NUM_PHASES = 16
 
 
 def _load() -> ctypes.CDLL:
@@ -96,6 +98,10 @@ def _load() -> ctypes.CDLL:
         "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
         "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                 ctypes.POINTER(vp), i32p], ctypes.c_int),
+        "dflash_ctx_set_persistent": ([vp, i32], ctypes.c_int),
+        "dflash_ctx_persistent_path": ([vp, i32, i32p], ctypes.c_int),
+        "dflash_ctx_check": ([vp, vp], ctypes.c_int),
+        "dflash_persist_trace": ([vp, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, i32p, i32p], ctypes.c_int),
         "dflash_profile_enable": ([vp, ctypes.c_uint32], ctypes.c_int),
         "dflash_profile_read": ([vp, ctypes.POINTER(ctypes.c_double), i64p], ctypes.c_int),
         "dflash_phase_name": ([i32], ctypes.c_char_p),
@@ -256,6 +262,38 @@ class Context:
                                                             ctypes.byref(k), ctypes.byref(v),
                                                             ctypes.byref(phys)))
         return c.value, k.value, v.value, phys.value
+
+    def set_persistent(self, enable: bool) -> None:
+        """dflash_ctx_set_persistent: the single-launch draft block on / off."""
+        _check("dflash_ctx_set_persistent", lib.dflash_ctx_set_persistent(self.handle, 1 if enable else 0))
+
+    def persistent_path(self, K: int) -> bool:
+        """dflash_ctx_persistent_path: whether a block of K rows per sequence
+        runs as one launch on this device."""
+        y = ctypes.c_int32()
+        _check("dflash_ctx_persistent_path", lib.dflash_ctx_persistent_path(self.handle, int(K), ctypes.byref(y)))
+        return bool(y.value)
+
+    def check(self, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """dflash_ctx_check: raises DFlashError if a single-launch block on
+        this context was abandoned (an expired barrier wait)."""
+        _check("dflash_ctx_check", lib.dflash_ctx_check(self.handle, _stream(stream)))
+
+    def persist_trace(self):
+        """dflash_persist_trace: the last profiled single-launch block's
+        timeline as a [workgroups, slots] uint64 array of 100 MHz ticks (or
+        None)."""
+        import numpy as np
+        nwg, stride = ctypes.c_int32(), ctypes.c_int32()
+        _check("dflash_persist_trace", lib.dflash_persist_trace(self.handle, None, 0, ctypes.byref(nwg),
+                                                                ctypes.byref(stride)))
+        if nwg.value == 0:
+            return None
+        out = np.zeros(nwg.value * stride.value, np.uint64)
+        _check("dflash_persist_trace",
+               lib.dflash_persist_trace(self.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                        out.size, ctypes.byref(nwg), ctypes.byref(stride)))
+        return out.reshape(nwg.value, stride.value)
 
     def profile(self, enable=True) -> None:
         """Time phases with HIP events: True = every phase, False = off, a

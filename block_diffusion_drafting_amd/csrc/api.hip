@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -54,6 +55,13 @@ struct Alloc {
   }
 };
 
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = atoi(v);
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
 int64_t next_pow2(int64_t n) {
   int64_t c = 1;
   while (c < n) c <<= 1;
@@ -74,6 +82,7 @@ struct dflash_model {
   double* inv_freq = nullptr;  // [d/2]
   std::vector<Packed> qkv, o, gu, down;
   Packed lm, fc, kv;
+  PLayer* players = nullptr;   // device [L]: the layer table of the persistent draft kernel
   int64_t layer_bytes = 0, lm_bytes = 0, proj_bytes = 0;
 
   const float* attn_gain(int l) const { return gains + (size_t)(2 * l) * cfg.hidden; }
@@ -88,11 +97,11 @@ struct Buf {
 
 enum Phase {
   PH_EMBED, PH_QKV, PH_ATTN, PH_O, PH_GU, PH_DOWN, PH_LM, PH_FINAL, PH_FC, PH_KV, PH_GROW, PH_ROWMAP,
-  PH_COMBINE, PH_RESID, PH_FCFIN
+  PH_COMBINE, PH_RESID, PH_FCFIN, PH_PERSIST
 };
 static const char* kPhaseNames[DFLASH_NUM_PHASES] = {
     "embed", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head", "finalize", "fc", "kv_inject",
-    "grow", "rowmap", "attn_combine", "resid_norm", "fc_finalize"};
+    "grow", "rowmap", "attn_combine", "resid_norm", "fc_finalize", "persistent_draft"};
 
 struct Profiler {
   uint32_t mask = 0;   // bit p: time phase p
@@ -122,6 +131,22 @@ struct dflash_ctx {
   // workspaces
   Buf x, ssq, q, bk, bvt, keys, part, attn_part, rowmap;
   Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
+  // persistent single-launch draft block (see persist.hip)
+  struct Persist {
+    bool enabled = false;   // opt in: measured slower than the per-product kernels
+    int nwg = 0;            // workgroups (compute units); 0 = not probed yet, -1 = unavailable
+    int down_splits = 8;
+    int pf_frags = 12;
+    int pf_att = 24;
+    unsigned epoch = 0;     // launches since the barrier flags were last cleared
+    int K = 0, max_splits = 0;   // shape the per-launch buffers were sized for
+    Buf scratch;            // activations of every layer and phase (one launch)
+    Buf apart;              // attention partials
+    Buf sync;               // counters, flags, error word (zeroed once)
+    size_t off_err = 0;     // byte offset of the error word in `sync`
+    Buf trace;              // timeline of the last profiled launch
+    int trace_nwg = 0, trace_stride = 0;
+  } pst;
 };
 
 namespace {
@@ -354,6 +379,23 @@ dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights
     }
     m->proj_bytes = packed_bytes(m->fc) + (L > 0 ? packed_bytes(m->kv) : 0);
   }
+  if (L > 0) {
+    std::vector<PLayer> tbl(L);
+    for (int l = 0; l < L; ++l) {
+      tbl[l].qkv = m->qkv[l];
+      tbl[l].o = m->o[l];
+      tbl[l].gu = m->gu[l];
+      tbl[l].down = m->down[l];
+      tbl[l].attn_gain = m->attn_gain(l);
+      tbl[l].mlp_gain = m->mlp_gain(l);
+    }
+    m->players = (PLayer*)m->alloc.get(sizeof(PLayer) * L);
+    if (!m->players) return cleanup(fail(DFLASH_E_ALLOC, "allocation failed"));
+    m->owned.push_back(m->players);
+    if (hipMemcpyAsync(m->players, tbl.data(), sizeof(PLayer) * L, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return cleanup(fail(DFLASH_E_HIP, "upload of the layer table failed"));
+  }
   *out = m;
   return DFLASH_OK;
 }
@@ -420,6 +462,7 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
     c->alloc.custom = true;
   }
   c->seq.assign(batch, DevSeq{});
+  c->pst.enabled = env_int("DFLASH_PERSISTENT", 0, 0, 1) != 0;
   c->seq_dev = (DevSeq*)c->alloc.get(sizeof(DevSeq) * batch);
   if (!c->seq_dev) {
     delete c;
@@ -454,7 +497,8 @@ dflash_status dflash_ctx_destroy(dflash_ctx* c) {
   }
   c->alloc.put(c->seq_dev);
   for (Buf* b : {&c->x, &c->ssq, &c->q, &c->bk, &c->bvt, &c->keys, &c->part, &c->attn_part, &c->rowmap,
-                 &c->xg_hi, &c->xg_lo, &c->o_hi, &c->o_lo, &c->act_hi, &c->act_lo, &c->c_hi, &c->c_lo})
+                 &c->xg_hi, &c->xg_lo, &c->o_hi, &c->o_lo, &c->act_hi, &c->act_lo, &c->c_hi, &c->c_lo,
+                 &c->pst.scratch, &c->pst.apart, &c->pst.sync, &c->pst.trace})
     c->alloc.put(b->p);
   delete c;
   return DFLASH_OK;
@@ -629,6 +673,177 @@ dflash_status dflash_project_ctx(dflash_ctx* c, const void* feats, const int32_t
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// persistent single-launch draft block (persist.hip): bf16 drafters whose
+// block has at most 16 rows in all
+// ---------------------------------------------------------------------------
+
+// Workgroups of the persistent kernel (one per compute unit), or -1 when
+// the device cannot run it (no cooperative launch, occupancy, grid shape).
+static int persist_nwg(dflash_ctx* c) {
+  auto& P = c->pst;
+  if (P.nwg != 0) return P.nwg;
+  P.nwg = -1;
+  P.pf_frags = env_int("DFLASH_PF_FRAGS", 12, 0, 48);
+  P.pf_att = env_int("DFLASH_PF_ATT", 2 * P.pf_frags, 0, 48);
+  P.down_splits = env_int("DFLASH_DOWN_SPLITS", 8, 1, 32);
+
+  int dev = 0, coop = 0, n = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return -1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (persist_occupancy(c->m->cfg.head_dim, &occ) != hipSuccess || occ < 1) return -1;
+  // the flag barrier reads at most 256 flags; the down projection's splits
+  // must divide the grid
+  if (n < 8 || n > 256 || n % P.down_splits) return -1;
+  P.nwg = n;
+  return n;
+}
+
+static bool persist_ok(dflash_ctx* c, int K) {
+  const dflash_config& cf = c->m->cfg;
+  if (!c->pst.enabled || cf.dtype != DFLASH_BF16 || cf.n_layers < 1) return false;
+  if ((int64_t)c->B * K > 16) return false;                       // one 16-row activation tile
+  if ((int64_t)(cf.n_q_heads / cf.n_kv_heads) * K > 64) return false;  // one query group per KV head
+  if (cf.head_dim != 64 && cf.head_dim != 128) return false;
+  if (cf.hidden > 4096) return false;                              // norm loads per thread
+  return persist_nwg(c) > 0;
+}
+
+static dflash_status persist_draft(dflash_ctx* c, const int32_t* ids, int K, int32_t* draft, float* logits,
+                                   void* hidden, hipStream_t s) {
+  const dflash_model* m = c->m;
+  const dflash_config& cf = m->cfg;
+  auto& P = c->pst;
+  const int B = c->B, H = cf.hidden, L = cf.n_layers, d = cf.head_dim, nq = cf.n_q_heads, nkv = cf.n_kv_heads;
+  const int nwg = P.nwg, S = P.down_splits;
+  const int Kpad = round_up(K, 64);
+  // attention: the smallest split length (a multiple of 64, at least 128)
+  // whose (sequence, KV head, split) units fit one round of the grid
+  int max_len = 0;
+  for (int b = 0; b < B; ++b) max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
+  int chunk = 128;
+  for (;; chunk += 64) {
+    int64_t units = 0;
+    for (int b = 0; b < B; ++b) units += (int64_t)nkv * ((c->seq[b].ctx_len + chunk - 1) / chunk + (K + chunk - 1) / chunk);
+    if (units <= nwg || chunk >= max_len + K) break;
+  }
+  int max_splits = 0;
+  for (int b = 0; b < B; ++b) {
+    const int ns = (c->seq[b].ctx_len + chunk - 1) / chunk + (K + chunk - 1) / chunk;
+    max_splits = ns > max_splits ? ns : max_splits;
+  }
+  const int nkb_h = H / 32, nkb_o = nq * d / 32, nkb_i = m->down[0].nkb, T_h = H / 16;
+  // per-launch buffers
+  auto al = [](size_t& off, size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  size_t off = 0;
+  al(off, (size_t)(2 * L + 1) * 16 * H * 4);                          // xs
+  const size_t o_xg = al(off, (size_t)(2 * L + 1) * 2 * nkb_h * BLOCK_BYTES);
+  const size_t o_ssq = al(off, (size_t)(2 * L + 1) * H * 4);
+  const size_t o_q = al(off, (size_t)L * 16 * nq * d * 2);
+  const size_t o_bk = al(off, (size_t)L * B * nkv * Kpad * d * 2);
+  const size_t o_bvt = al(off, (size_t)L * B * nkv * Kpad * d * 2);
+  const size_t o_of = al(off, (size_t)L * 2 * nkb_o * BLOCK_BYTES);
+  const size_t o_act = al(off, (size_t)L * 2 * nkb_i * BLOCK_BYTES);
+  const size_t o_dp = al(off, (size_t)L * S * T_h * 256 * 4);
+  dflash_status st;
+  if (P.scratch.bytes < off || !P.scratch.p) {
+    if ((st = ensure(c->alloc, P.scratch, off))) return st;
+    // zero: the k-block padding of the SwiGLU output is never written
+    HIP_TRY(launch_fill_u32((unsigned*)P.scratch.p, P.scratch.bytes / 4, 0u, s));
+  }
+  const size_t apart_bytes = (size_t)L * B * nkv * max_splits * 4 * (d * 16 + 32) * 4;
+  if ((st = ensure(c->alloc, P.apart, apart_bytes))) return st;
+  size_t soff = 0;
+  const size_t o_keys = al(soff, 16 * 8);
+  const size_t o_acnt = al(soff, (size_t)L * B * nkv * 4);
+  const size_t o_dcnt = al(soff, (size_t)L * T_h * 4);
+  const size_t o_lm = al(soff, 4);
+  const size_t o_err = al(soff, 4);
+  const size_t o_flags = al(soff, (size_t)nwg * 4);
+  if (P.sync.bytes < soff || !P.sync.p) {
+    if ((st = ensure(c->alloc, P.sync, soff))) return st;
+    HIP_TRY(launch_fill_u32((unsigned*)P.sync.p, P.sync.bytes / 4, 0u, s));
+    P.epoch = 0;
+  }
+  P.off_err = o_err;
+  uint8_t* sb = (uint8_t*)P.scratch.p;
+  uint8_t* yb = (uint8_t*)P.sync.p;
+  PArgs a{};
+  a.layers = m->players;
+  a.lm = m->lm;
+  a.embed = (const bf16_t*)m->embed;
+  a.final_gain = m->final_gain();
+  a.inv_freq = m->inv_freq;
+  a.seqs = c->seq_dev;
+  a.ids = ids;
+  a.draft = draft;
+  a.logits = logits;
+  a.hidden = hidden;
+  a.B = B;
+  a.K = K;
+  a.M = B * K;
+  a.H = H;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.d = d;
+  a.I = cf.intermediate;
+  a.V = cf.vocab;
+  a.L = L;
+  a.Kpad = Kpad;
+  a.nkb_i = nkb_i;
+  a.eps = (float)cf.rms_eps;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  a.chunk = chunk;
+  a.max_splits = max_splits;
+  a.down_splits = S;
+  a.pf_frags = P.pf_frags;
+  a.pf_att = P.pf_att;
+  a.xs = (float*)sb;
+  a.xg = (u32x4*)(sb + o_xg);
+  a.ssq = (float*)(sb + o_ssq);
+  a.q = (f16_t*)(sb + o_q);
+  a.bk = (f16_t*)(sb + o_bk);
+  a.bvt = (f16_t*)(sb + o_bvt);
+  a.apart = (float*)P.apart.p;
+  a.of = (u32x4*)(sb + o_of);
+  a.act = (u32x4*)(sb + o_act);
+  a.dpart = (float*)(sb + o_dp);
+  a.keys = (unsigned long long*)(yb + o_keys);
+  a.acnt = (unsigned*)(yb + o_acnt);
+  a.dcnt = (unsigned*)(yb + o_dcnt);
+  a.lmcnt = (unsigned*)(yb + o_lm);
+  a.err = (unsigned*)(yb + o_err);
+  a.flags = (unsigned*)(yb + o_flags);
+  a.base = P.epoch * persist_steps(L);
+  if (c->prof.mask >> PH_PERSIST & 1u) {
+    // timeline of this launch (profiling only)
+    const int stride = 8 * ((int)persist_steps(L) + 1);
+    if ((st = ensure(c->alloc, P.trace, (size_t)nwg * stride * 8))) return st;
+    HIP_TRY(launch_fill_u32((unsigned*)P.trace.p, (size_t)nwg * stride * 2, 0u, s));
+    a.trace = (unsigned long long*)P.trace.p;
+    a.trace_stride = stride;
+    P.trace_nwg = nwg;
+    P.trace_stride = stride;
+  }
+  {
+    PhaseTimer tm(c, PH_PERSIST, s);
+    const hipError_t e = launch_persist_draft(a, nwg, s);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DFLASH_E_HIP, "persistent draft launch failed: %s", hipGetErrorString(e));
+    }
+  }
+  P.epoch += 1;
+  P.K = K;
+  P.max_splits = max_splits;
+  return DFLASH_OK;
+}
+
 // Context rows of a fused step: projected features in the QKV activation
 // matrix from m-tile mt0 on, row map in the context's row-map buffer.
 struct FusedCtx {
@@ -641,6 +856,7 @@ template <typename T>
 static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_t* draft, float* logits,
                                 void* hidden, hipStream_t s, const FusedCtx& fused = FusedCtx{}) {
   using CT = typename CacheOf<T>::type;
+  if (fused.n_ctx == 0 && persist_ok(c, K)) return persist_draft(c, ids, K, draft, logits, hidden, s);
   const dflash_model* m = c->m;
   const dflash_config& cf = m->cfg;
   const int B = c->B, M = B * K, H = cf.hidden, L = cf.n_layers, d = cf.head_dim;
@@ -795,7 +1011,7 @@ static dflash_status step_impl(dflash_ctx* c, const void* feats, const int32_t* 
   const int mtb = (B * K + 15) / 16, mtc = (total + 15) / 16;
   dflash_status st;
   if (total == 0) return draft_impl<T>(c, ids, K, draft, logits, hidden, s);
-  if (m->cfg.n_layers == 0 || mtb + mtc > 4) {
+  if (m->cfg.n_layers == 0 || mtb + mtc > 4 || persist_ok(c, K)) {
     if ((st = project_impl<T>(c, feats, n_new, nullptr, s))) return st;
     return draft_impl<T>(c, ids, K, draft, logits, hidden, s);
   }
@@ -854,6 +1070,48 @@ dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* block_ids, int32_
   hipStream_t s = (hipStream_t)stream;
   return c->m->cfg.dtype == DFLASH_BF16 ? draft_impl<bf16_t>(c, block_ids, K, draft_ids, logits, hidden, s)
                                         : draft_impl<float>(c, block_ids, K, draft_ids, logits, hidden, s);
+}
+
+dflash_status dflash_ctx_set_persistent(dflash_ctx* c, int32_t enable) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  c->pst.enabled = enable != 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_ctx_persistent_path(dflash_ctx* c, int32_t K, int32_t* yes) {
+  if (!c || !yes) return fail(DFLASH_E_ARG, "NULL pointer");
+  if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
+  *yes = persist_ok(c, K) ? 1 : 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_ctx_check(dflash_ctx* c, void* stream) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  auto& P = c->pst;
+  if (!P.sync.p) return DFLASH_OK;
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  unsigned err = 0;
+  HIP_TRY(hipMemcpy(&err, (uint8_t*)P.sync.p + P.off_err, 4, hipMemcpyDeviceToHost));
+  if (err) {
+    HIP_TRY(hipMemset(P.sync.p, 0, P.sync.bytes));
+    HIP_TRY(hipDeviceSynchronize());
+    P.epoch = 0;
+    return fail(DFLASH_E_HIP, "persistent draft kernel: a barrier wait expired; outputs since the last check are invalid");
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_persist_trace(dflash_ctx* c, uint64_t* out, int64_t capacity, int32_t* nwg, int32_t* stride) {
+  if (!c || !nwg || !stride) return fail(DFLASH_E_ARG, "NULL pointer");
+  auto& P = c->pst;
+  *nwg = P.trace.p ? P.trace_nwg : 0;
+  *stride = P.trace.p ? P.trace_stride : 0;
+  const int64_t n = (int64_t)*nwg * *stride;
+  if (n == 0 || !out) return DFLASH_OK;   // size query
+  if (capacity < n) return fail(DFLASH_E_ARG, "capacity %lld < %lld", (long long)capacity, (long long)n);
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(out, P.trace.p, (size_t)n * 8, hipMemcpyDeviceToHost));
+  return DFLASH_OK;
 }
 
 dflash_status dflash_profile_enable(dflash_ctx* c, uint32_t phase_mask) {

@@ -175,6 +175,62 @@ hipError_t launch_grow_copy(DevSeq oldv, DevSeq newv, int L, int nkv, int d, int
                             hipStream_t s);
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// persistent single-launch draft block (bf16 drafters, batch * K <= 16)
+// ---------------------------------------------------------------------------
+struct PLayer {
+  Packed qkv, o, gu, down;
+  const float* attn_gain;
+  const float* mlp_gain;
+};
+
+struct PArgs {
+  const PLayer* layers;      // device [L]
+  Packed lm;
+  const bf16_t* embed;       // [V][H]
+  const float* final_gain;
+  const double* inv_freq;    // [d/2]
+  const DevSeq* seqs;
+  const int32_t* ids;        // [M]
+  int32_t* draft;            // [M]
+  float* logits;             // [M][V] or null
+  void* hidden;              // [M][H] bf16 or null
+  int32_t B, K, M, H, nq, nkv, d, I, V, L, Kpad, nkb_i;
+  float eps, scale_log2;
+  int32_t chunk, max_splits; // attention: keys per split, splits per (sequence, head)
+  int32_t down_splits;       // k-splits of the down projection (divides the grid)
+  int32_t pf_frags;          // warm-up fragments per wave share at a barrier
+  int32_t pf_att;            // the same at the barrier before attention
+  // per-launch buffers, one copy per layer / phase (16 activation rows)
+  float* xs;                 // [2L+1][16][H]          residual versions
+  u32x4* xg;                 // [2L+1][hi, lo][H/32][64] normed-input frags
+  float* ssq;                // [2L+1][H/16][16]       sums of squares
+  f16_t* q;                  // [L][16][nq*d]
+  f16_t* bk;                 // [L][B][nkv][Kpad][d]
+  f16_t* bvt;                // [L][B][nkv][d][Kpad]
+  float* apart;              // [L][B*nkv*max_splits][4][d*16 + 32]
+  u32x4* of;                 // [L][hi, lo][nq*d/32][64]
+  u32x4* act;                // [L][hi, lo][nkb_i][64]
+  float* dpart;              // [L][down_splits][H/16][64][4]
+  unsigned long long* keys;  // [16]
+  unsigned* acnt;            // [L][B*nkv]  split counters (self-resetting)
+  unsigned* dcnt;            // [L][H/16]   down split counters (self-resetting)
+  unsigned* lmcnt;           // [1]
+  unsigned* flags;           // [grid]      barrier flags (monotone)
+  unsigned* err;             // nonzero: a wait expired
+  unsigned base;             // flag value before this launch's first step
+  // optional timeline (null = off): per workgroup, 8 slots per phase
+  // (embed, 5 per layer, LM head) of the constant 100 MHz clock: [0] start,
+  // [1]-[5] marks inside the phase, [6] arrival at the barrier that ends it
+  // (the LM head: end of work), [7] that barrier's release
+  unsigned long long* trace;
+  int32_t trace_stride;
+};
+// barrier steps of one launch with L layers
+unsigned persist_steps(int L);
+hipError_t persist_occupancy(int d, int* blocks_per_cu);
+hipError_t launch_persist_draft(const PArgs& a, int nwg, hipStream_t s);
+
 // Frag-layout slot (16-byte unit index) of element (m, k) and its position
 // `e` inside the fragment.
 template <typename T>

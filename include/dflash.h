@@ -222,18 +222,52 @@ dflash_status dflash_ctx_buffers(const dflash_ctx *c, int32_t b, const void **ct
                                  const void **k_cache, const void **v_cache,
                                  int32_t *phys_rows);
 
+/* Single-launch draft block.  For bf16 drafters whose block has at most 16
+ * rows in all (batch * K <= 16) and at most 64 query rows per KV head
+ * ((n_q_heads / n_kv_heads) * K <= 64), dflash_draft_block runs a4-a9 as one
+ * cooperative launch of one workgroup per compute unit, with the same
+ * arithmetic as the per-product kernels up to summation order (kongchang.com,
+ * "System architecture": one forward per block; the launch keeps the weight
+ * stream going across the dependencies between products).  Its grid
+ * barriers wait at most about 2 s each; an expired wait abandons the launch
+ * and is reported by dflash_ctx_check.  In dflash_step the appended
+ * positions then go through dflash_project_ctx before the block.
+ *   dflash_ctx_set_persistent   enable or disable (default) the path for c;
+ *                               the environment variable DFLASH_PERSISTENT=1
+ *                               enables it for contexts created afterwards.
+ *   dflash_ctx_persistent_path  *yes = 1 if a block of K rows per sequence
+ *                               takes the path on this device, else 0.
+ *   dflash_ctx_check            waits for `stream`, then returns DFLASH_E_HIP
+ *                               if a launch on c was abandoned since the last
+ *                               check (its outputs are invalid; the barrier
+ *                               state is reset), else DFLASH_OK. */
+dflash_status dflash_ctx_set_persistent(dflash_ctx *c, int32_t enable);
+dflash_status dflash_ctx_persistent_path(dflash_ctx *c, int32_t K, int32_t *yes);
+dflash_status dflash_ctx_check(dflash_ctx *c, void *stream);
+
 /* Per-kernel timing with HIP events recorded on the call's stream around
  * every launch of dflash_project_ctx / dflash_draft_block that belongs to a
  * phase selected by dflash_profile_enable (bit p of phase_mask selects phase
  * p; 0 turns timing off; bits past the last phase are ignored).
  * Phases (index: name): 0 embed, 1 qkv, 2 attention, 3 o_proj, 4 gate_up,
  * 5 down, 6 lm_head, 7 finalize, 8 fc, 9 kv_inject, 10 grow, 11 rowmap,
- * 12 attn_combine, 13 resid_norm, 14 fc_finalize.
+ * 12 attn_combine, 13 resid_norm, 14 fc_finalize, 15 persistent_draft (the
+ * whole draft block as one launch, see dflash_ctx_set_persistent).
  * dflash_profile_read waits for the recorded events, adds their durations
  * (milliseconds) and launch counts per phase into ms[] / count[] (host
  * arrays of DFLASH_NUM_PHASES entries, overwritten) and clears the record. */
-#define DFLASH_NUM_PHASES 15
+#define DFLASH_NUM_PHASES 16
 dflash_status dflash_profile_enable(dflash_ctx *c, uint32_t phase_mask);
+/* Timeline of the last single-launch draft block run while phase 15 was
+ * selected: *nwg workgroups x *stride slots (host out [nwg * stride] uint64,
+ * capacity entries), ticks of the GPU's constant 100 MHz clock per
+ * workgroup, 8 slots per phase (embed, then qkv, attention, o_proj, gate_up,
+ * down per layer, then lm_head): 0 start, 1-5 marks inside the phase, 6
+ * arrival at the barrier that ends it (lm_head: end of work), 7 release;
+ * unwritten slots are 0.  *nwg = 0 if none was recorded; out = NULL only returns the sizes.
+ * Waits for the device. */
+dflash_status dflash_persist_trace(dflash_ctx *c, uint64_t *out, int64_t capacity, int32_t *nwg,
+                                   int32_t *stride);
 dflash_status dflash_profile_read(dflash_ctx *c, double *ms, int64_t *count);
 const char *dflash_phase_name(int32_t phase);
 
