@@ -131,6 +131,11 @@ struct dflash_ctx {
   // workspaces
   Buf x, ssq, q, bk, bvt, keys, part, attn_part, rowmap;
   Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
+  // L2 warm-up by the spare blocks of latency-bound kernels (fragments per
+  // product wave): output projection, next QKV, LM head
+  int warm_o = 16, warm_qkv = 12, warm_lm = 2;
+  // attention grid: 8-wave workgroup equivalents per compute unit
+  int attn_wgs_per_cu = 2;
   // persistent single-launch draft block (see persist.hip)
   struct Persist {
     bool enabled = false;   // opt in: measured slower than the per-product kernels
@@ -463,6 +468,10 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
   }
   c->seq.assign(batch, DevSeq{});
   c->pst.enabled = env_int("DFLASH_PERSISTENT", 0, 0, 1) != 0;
+  c->warm_o = env_int("DFLASH_WARM_O", c->warm_o, 0, 64);
+  c->warm_qkv = env_int("DFLASH_WARM_QKV", c->warm_qkv, 0, 64);
+  c->warm_lm = env_int("DFLASH_WARM_LM", c->warm_lm, 0, 64);
+  c->attn_wgs_per_cu = env_int("DFLASH_ATTN_WGS_PER_CU", c->attn_wgs_per_cu, 1, 16);
   c->seq_dev = (DevSeq*)c->alloc.get(sizeof(DevSeq) * batch);
   if (!c->seq_dev) {
     delete c;
@@ -568,6 +577,27 @@ static dflash_status run_gemm(dflash_ctx* c, int phase, int epi, const Packed& W
   }
   if (plan_out) *plan_out = p;
   return DFLASH_OK;
+}
+
+// Warm-up descriptor for the product `epi` over W with M activation rows,
+// planned exactly as run_gemm will launch it (see Warm in kernels.h);
+// `frags` weight fragments per product wave (0 = none).
+template <typename T>
+static Warm make_warm(int epi, const Packed& W, int M, int frags, bool force_split = false) {
+  Warm w{};
+  if (frags <= 0) return w;
+  GemmPlan p = plan_gemm(epi, W, M, sizeof(T) == 2, false);
+  (void)force_split;   // the hi/lo choice does not change which weights a workgroup reads
+  w.w = W.w;
+  w.nkb = W.nkb;
+  w.n_tiles = W.n_tiles;
+  w.n_groups = p.n_groups;
+  w.nsplit = p.nsplit;
+  w.kbu = p.kbu;
+  w.waves = p.fixed ? 4 : (p.mtt == 4 ? 4 : 8);
+  w.frags = frags;
+  w.consumers = p.n_groups * p.nsplit;
+  return w;
 }
 
 // (a2) growth: a sequence whose append would overflow its capacity gets
@@ -887,7 +917,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   // split length, sets the cost of the combine.
   const int qg_per_wg = qgroups > 1 ? 2 : 1;
   const int64_t wg_per_split = (int64_t)nkv * ((qgroups + qg_per_wg - 1) / qg_per_wg);
-  const int64_t round_wgs = qg_per_wg == 1 ? 512 : 256;
+  const int64_t round_wgs = (qg_per_wg == 1 ? 2 : 1) * (int64_t)c->attn_wgs_per_cu * 256;
   int chunk = 128;
   for (;; chunk += 64) {
     int64_t wgs = 0;
@@ -951,6 +981,8 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
       return st;
     }
     a.layer = l;
+    // the attention kernel's spare blocks warm the output projection's weights
+    a.warm = make_warm<T>(mtiles == 1 ? EPI_RESNORM : EPI_PART, m->o[l], M, c->warm_o);
     {
       PhaseTimer tm(c, PH_ATTN, s);
       HIP_TRY(launch_attention<CT>(a, s));
@@ -983,8 +1015,13 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
     if ((st = run_gemm<T>(c, PH_DOWN, EPI_PART, m->down[l], af, nullptr, 0, M, e, s, &p))) return st;
     {
       PhaseTimer tm(c, PH_RESID, s);
+      // and the next product's weights (the next layer's QKV, or the LM head)
+      const Warm wn = l + 1 < L ? make_warm<T>(EPI_QKV, m->qkv[l + 1],
+                                               fused.n_ctx > 0 ? fused.mt0 * 16 + fused.n_ctx : M, c->warm_qkv)
+                                : make_warm<T>(EPI_ARGMAX, m->lm, M, c->warm_lm);
       HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
-                                   l + 1 < L ? m->attn_gain(l + 1) : m->final_gain(), xg, (float*)c->ssq.p, s));
+                                   l + 1 < L ? m->attn_gain(l + 1) : m->final_gain(), xg, (float*)c->ssq.p, s,
+                                   wn));
     }
   }
   (void)none;

@@ -35,8 +35,10 @@ size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d) {
   return (size_t)B * nkv * qgroups * max_splits * 4 * (d * 16 + 32);
 }
 
+// Two waves per SIMD (two 4-wave or one 8-wave workgroup per compute unit,
+// as the grid is planned): at most 256 registers per wave.
 template <typename T, int D, int QG>
-__global__ __launch_bounds__(256 * QG) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnArgs a) {
   using E = Elem<T>;
   constexpr int CHUNK_KEYS = chunk_keys<T, D>();
   constexpr int ES = sizeof(T);
@@ -56,6 +58,12 @@ __global__ __launch_bounds__(256 * QG) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kl[2][CHUNK_KEYS * KROW];
   __shared__ __attribute__((aligned(16))) uint8_t vl[2][D * VROW];
 
+  // appended workgroups warm the output projection's weights instead
+  if (a.warm.w && (int)blockIdx.x >= a.warm.first) {
+    warm_consumer(a.warm, (int)blockIdx.x - a.warm.first, 4 * QG, (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63),
+                  (lds_void_t*)(kl[0] + (threadIdx.x >> 6) * 1024));
+    return;
+  }
   // QG query groups share each staged chunk: wave w is query tile w % 4 of
   // query group qgp * QG + w / 4
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
@@ -119,17 +127,21 @@ __global__ __launch_bounds__(256 * QG) void attention_kernel(AttnArgs a) {
   for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Chunk staging through registers: the global loads of chunk c+1 are in
-  // flight while chunk c is computed from LDS.  Keys at or past the split
-  // end load as zero (K rows and V^T columns).
-  u32x4 kr[KPT], vr[VPT];
-  auto gload = [&](int c0, int cend) {
+  // Chunk staging through registers, two chunks in flight: while chunk c
+  // is computed from LDS, the loads of chunks c+1 and c+2 are outstanding
+  // in two register sets; chunk c+1 is stored to the other LDS buffer once
+  // c is done.  Keys at or past the split end load as zero (K rows and V^T
+  // columns).
+  struct Regs {
+    u32x4 kr[KPT], vr[VPT];
+  };
+  auto gload = [&](Regs& rg, int c0, int cend) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int t = threadIdx.x + j * NTH;
       const int row = t / KP_ROW, pc = t % KP_ROW;
-      kr[j] = (c0 + row < cend) ? gld16((const uint8_t*)(kbase + (size_t)(c0 + row) * D) + pc * 16)
-                                : u32x4{0u, 0u, 0u, 0u};
+      rg.kr[j] = (c0 + row < cend) ? gld16((const uint8_t*)(kbase + (size_t)(c0 + row) * D) + pc * 16)
+                                   : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -146,34 +158,25 @@ __global__ __launch_bounds__(256 * QG) void attention_kernel(AttnArgs a) {
         for (int e2 = 0; e2 < EPP; ++e2) tmp[e2] = (key + e2 < cend) ? gld(src + e2) : (T)0;
         v = *(const u32x4*)tmp;
       }
-      vr[j] = v;
+      rg.vr[j] = v;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const Regs& rg, int buf) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int t = threadIdx.x + j * NTH;
-      *(u32x4*)(kl[buf] + (t / KP_ROW) * KROW + (t % KP_ROW) * 16) = kr[j];
+      *(u32x4*)(kl[buf] + (t / KP_ROW) * KROW + (t % KP_ROW) * 16) = rg.kr[j];
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int t = threadIdx.x + j * NTH;
-      *(u32x4*)(vl[buf] + (t / VP_ROW) * VROW + (t % VP_ROW) * 16) = vr[j];
+      *(u32x4*)(vl[buf] + (t / VP_ROW) * VROW + (t % VP_ROW) * 16) = rg.vr[j];
     }
   };
-
-  const int nchunks = (k1 - k0 + CHUNK_KEYS - 1) / CHUNK_KEYS;
-  gload(k0, min(k1, k0 + CHUNK_KEYS));
-  lstore(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int c0 = k0 + c * CHUNK_KEYS;
-    const int cend = min(k1, c0 + CHUNK_KEYS);
-    const int buf = c & 1;
-    if (c + 1 < nchunks) gload(c0 + CHUNK_KEYS, min(k1, c0 + 2 * CHUNK_KEYS));
+  // online softmax and P.V over chunk [c0, cend) held in LDS buffer buf
+  auto compute = [&](int c0, int cend, int buf) {
     const uint8_t* klb = kl[buf];
     const uint8_t* vlb = vl[buf];
-
 #pragma unroll
     for (int sub = 0; sub < CHUNK_KEYS / KP; ++sub) {
       const int kb = sub * KP;  // key offset of this P.V step within the chunk
@@ -243,7 +246,42 @@ __global__ __launch_bounds__(256 * QG) void attention_kernel(AttnArgs a) {
         o[t] = E::mma(vf, pf, o[t]);
       }
     }
-    if (c + 1 < nchunks) lstore(buf ^ 1);
+  };
+  auto chunk_range = [&](int c, int& c0, int& cend) {
+    c0 = k0 + c * CHUNK_KEYS;
+    cend = min(k1, c0 + CHUNK_KEYS);
+  };
+
+  const int nchunks = (k1 - k0 + CHUNK_KEYS - 1) / CHUNK_KEYS;
+  Regs r0, r1;
+  int c0, cend;
+  chunk_range(0, c0, cend);
+  gload(r0, c0, cend);
+  if (nchunks > 1) {
+    chunk_range(1, c0, cend);
+    gload(r1, c0, cend);
+  }
+  lstore(r0, 0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    // chunk c in LDS buffer 0, chunk c+1 in flight in r1
+    if (c + 2 < nchunks) {
+      chunk_range(c + 2, c0, cend);
+      gload(r0, c0, cend);
+    }
+    chunk_range(c, c0, cend);
+    compute(c0, cend, 0);
+    if (c + 1 < nchunks) lstore(r1, 1);
+    __syncthreads();
+    if (c + 1 >= nchunks) break;
+    // chunk c+1 in LDS buffer 1, chunk c+2 in flight in r0
+    if (c + 3 < nchunks) {
+      chunk_range(c + 3, c0, cend);
+      gload(r1, c0, cend);
+    }
+    chunk_range(c + 1, c0, cend);
+    compute(c0, cend, 1);
+    if (c + 2 < nchunks) lstore(r0, 0);
     __syncthreads();
   }
   l_run = wave_xor_sum16_32(l_run);
@@ -356,11 +394,17 @@ static unsigned attn_grid(const AttnArgs& a, int qg_per_wg) {
 }
 
 template <typename T>
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a_in, hipStream_t s) {
+  AttnArgs a = a_in;
   // two query groups per workgroup (eight waves) whenever there are several:
   // each staged K/V chunk then serves 128 query rows
-  const int QG = a.qgroups > 1 ? 2 : 1;
-  dim3 grid(attn_grid(a, QG));
+  const int QG = a_in.qgroups > 1 ? 2 : 1;
+  unsigned nblk = attn_grid(a, QG);   // a multiple of 8
+  if (a.warm.w) {
+    a.warm.first = (int)nblk;
+    nblk += (unsigned)a.warm.consumers;
+  }
+  dim3 grid(nblk);
   switch (a.d * 4 + QG) {
     case 64 * 4 + 1: hipLaunchKernelGGL((attention_kernel<T, 64, 1>), grid, dim3(256), 0, s, a); break;
     case 64 * 4 + 2: hipLaunchKernelGGL((attention_kernel<T, 64, 2>), grid, dim3(512), 0, s, a); break;

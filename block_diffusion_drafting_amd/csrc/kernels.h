@@ -116,7 +116,49 @@ hipError_t launch_gemm(int epi, const GemmPlan& p, const GemmArgs& g, const EpiA
 template <typename T, int EPI>
 hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 
+// L2 warm-up of a later product's weights by extra workgroups appended to
+// a latency-bound kernel's grid.  Workgroups are dealt to the eight XCDs
+// round robin by block index, so warm-up workgroup k (block first + k,
+// first a multiple of 8) sits on the XCD of the product's workgroup k and
+// loads, into that XCD's L2, the first `frags` weight fragments each of
+// its waves will read (k-block major, then tile; data discarded).
+struct Warm {
+  const uint8_t* w;            // packed weights; null = no warm-up
+  int32_t nkb, n_tiles;
+  int32_t n_groups, nsplit, kbu;
+  int32_t waves;               // waves per product workgroup
+  int32_t frags;               // fragments per product wave
+  int32_t consumers;           // product workgroups to warm for (m-group 0)
+  int32_t first;               // block index of the first warm-up workgroup
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Warm-up workgroup k with nw waves (this is wave `wave`): product
+// workgroup k's waves cw = wave, wave + nw, ... ; `slot` is this wave's own
+// 1 KiB of LDS.  Waits for its loads before returning.
+__device__ __forceinline__ void warm_consumer(const Warm& m, int k, int nw, int wave, int lane, lds_void_t* slot) {
+  if (k >= m.consumers) return;
+  const int s = k % m.nsplit;
+  const int ng = (k / m.nsplit) % m.n_groups;
+  const int tile0 = (int)((long)ng * m.n_tiles / m.n_groups);
+  const int nt = (int)((long)(ng + 1) * m.n_tiles / m.n_groups) - tile0;
+  const int kbA = s * m.kbu, kbB = min(m.nkb, kbA + m.kbu);
+  const int per = (kbB - kbA + m.waves - 1) / m.waves;
+  const uint8_t* base = m.w + (size_t)lane * FRAG_BYTES;
+  for (int cw = wave; cw < m.waves; cw += nw) {
+    const int k0 = kbA + cw * per, k1 = min(kbB, k0 + per);
+    int cnt = 0;
+    for (int kb = k0; kb < k1 && cnt < m.frags; ++kb)
+      for (int t = 0; t < nt && cnt < m.frags; ++t, ++cnt)
+        __builtin_amdgcn_global_load_lds((const void*)(base + ((size_t)(tile0 + t) * m.nkb + kb) * BLOCK_BYTES), slot,
+                                         16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 struct AttnArgs {
+  Warm warm;              // weights of the output projection that follows
   const void* q;
   const void* bk;
   const void* bvt;
@@ -141,7 +183,8 @@ hipError_t launch_embed(const int32_t* ids, const void* embed, const float* gain
 // x += sum of split-K partials (fixed order); xg = x * gain -> frag; ssq.
 template <typename T>
 hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
-                             const float* gain, Frag xg, float* ssq, hipStream_t s);
+                             const float* gain, Frag xg, float* ssq, hipStream_t s,
+                             const Warm& warm = Warm{});
 // Rows of one context append: rows [start[b], start[b+1]) belong to
 // sequence b and go to slots ctx0[b] + (row - start[b]) (host values).
 struct RowInfo {

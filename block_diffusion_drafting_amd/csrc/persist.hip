@@ -37,8 +37,6 @@
 
 namespace dflash {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 namespace {
 
 constexpr int PW = 8;        // waves per workgroup
