@@ -12,6 +12,7 @@ Entry points keep the C names:
   dflash_project_ctx               (a1)-(a3) project + append + KV injection
   dflash_draft_block               (a4)-(a9) one non-causal draft forward
   dflash_accept                    (a10) greedy acceptance
+  dflash_decay_ce                  loss-decay weighted cross-entropy (training)
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdflash.so")
 
 DFLASH_F32, DFLASH_BF16 = 0, 1
 MAX_BATCH, MAX_K = 256, 1024
+DECAY_CE_WORKSPACE = 256
 
 
 class DFlashError(RuntimeError):
@@ -65,7 +67,7 @@ class _Allocator(ctypes.Structure):
 EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_model_create",
            "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
            "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_step",
-           "dflash_accept",
+           "dflash_accept", "dflash_decay_ce",
            "dflash_ctx_query", "dflash_ctx_buffers", "dflash_ctx_set_persistent",
            "dflash_ctx_persistent_path", "dflash_ctx_check", "dflash_persist_trace",
            "dflash_profile_enable",
@@ -95,6 +97,8 @@ def _load() -> ctypes.CDLL:
         "dflash_draft_block": ([vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
         "dflash_step": ([vp, vp, ctypes.POINTER(ctypes.c_int32), vp, i32, vp, vp, vp, vp], ctypes.c_int),
         "dflash_accept": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
+        "dflash_decay_ce": ([vp, ctypes.c_int, vp, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp, vp],
+                            ctypes.c_int),
         "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
         "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                 ctypes.POINTER(vp), i32p], ctypes.c_int),
@@ -382,6 +386,40 @@ def dflash_accept(draft_ids: torch.Tensor, target_ids: torch.Tensor, batch: int,
         raise ValueError("shape mismatch")
     _check("dflash_accept", lib.dflash_accept(_ptr(draft_ids), _ptr(target_ids), int(batch), int(K),
                                               _ptr(accept_len), _stream(stream)))
+
+
+def dflash_decay_ce(logits: torch.Tensor, targets: torch.Tensor, block: int, gamma: float,
+                    loss: torch.Tensor, ce: torch.Tensor, grad: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Loss-decay weighted cross-entropy of logits [rows, vocab] (float32 or
+    bfloat16): loss [1] float32, per-row ce [rows] float32 and, if given,
+    grad [rows, vocab] in the logits' dtype.  workspace: a device tensor of
+    at least DECAY_CE_WORKSPACE bytes (allocated here if None)."""
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, vocab] tensor")
+    if logits.dtype == torch.bfloat16:
+        dt = DFLASH_BF16
+    elif logits.dtype == torch.float32:
+        dt = DFLASH_F32
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    rows, vocab = logits.shape
+    if targets.dtype != torch.int32 or targets.numel() != rows:
+        raise ValueError("targets must be int32 [rows]")
+    if loss.dtype != torch.float32 or loss.numel() < 1 or ce.dtype != torch.float32 or ce.numel() != rows:
+        raise ValueError("loss [1] and ce [rows] must be float32")
+    if grad is not None and (grad.dtype != logits.dtype or grad.shape != logits.shape or
+                             not grad.is_contiguous()):
+        raise ValueError("grad must match logits")
+    if workspace is None:
+        workspace = torch.empty(DECAY_CE_WORKSPACE, dtype=torch.uint8, device=logits.device)
+    elif workspace.numel() * workspace.element_size() < DECAY_CE_WORKSPACE:
+        raise ValueError("workspace too small")
+    _check("dflash_decay_ce",
+           lib.dflash_decay_ce(_ptr(logits), dt, _ptr(targets), int(rows), int(vocab), int(block),
+                               float(gamma), _ptr(loss), _ptr(ce), _ptr(grad), _ptr(workspace),
+                               _stream(stream)))
 
 
 def version() -> str:

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -1187,6 +1188,22 @@ dflash_status dflash_accept(const int32_t* draft_ids, const int32_t* target_ids,
   if (batch < 1 || batch > (1 << 20)) return fail(DFLASH_E_ARG, "batch = %d out of range", batch);
   if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
   HIP_TRY(launch_accept(draft_ids, target_ids, batch, K, accept_len, (hipStream_t)stream));
+  return DFLASH_OK;
+}
+
+dflash_status dflash_decay_ce(const void* logits, dflash_dtype dtype, const int32_t* targets, int32_t rows,
+                              int32_t vocab, int32_t block, double gamma, float* loss, float* ce, void* grad,
+                              void* workspace, void* stream) {
+  if (!loss || !workspace) return fail(DFLASH_E_ARG, "NULL pointer");
+  if (rows > 0 && (!logits || !targets || !ce)) return fail(DFLASH_E_ARG, "NULL pointer");
+  if ((uintptr_t)workspace % 8) return fail(DFLASH_E_ARG, "workspace not 8-byte aligned");
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "dtype = %d", (int)dtype);
+  if (rows < 0) return fail(DFLASH_E_ARG, "rows = %d", rows);
+  if (vocab < 1) return fail(DFLASH_E_ARG, "vocab = %d", vocab);
+  if (block < 1) return fail(DFLASH_E_ARG, "block = %d", block);
+  if (!(gamma > 0.0) || !std::isfinite(gamma)) return fail(DFLASH_E_ARG, "gamma = %g", gamma);
+  HIP_TRY(launch_decay_ce(logits, (int)dtype, targets, rows, vocab, block, gamma, loss, ce, rows > 0 ? grad : nullptr,
+                          (double*)workspace, (hipStream_t)stream));
   return DFLASH_OK;
 }
 

@@ -205,6 +205,10 @@ hipError_t launch_finalize(const unsigned long long* keys, int M, int32_t* draft
                            void* hidden, hipStream_t s);
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int K,
                          int32_t* out, hipStream_t s);
+// Loss-decay weighted cross-entropy (loss.hip); wsum is one device double.
+hipError_t launch_decay_ce(const void* logits, int dtype, const int32_t* targets, int R, int V, int block,
+                           double gamma, float* loss, float* ce, void* grad, double* wsum, hipStream_t s);
+int decay_ce_resident_max(int elem_bytes);
 template <typename T>
 hipError_t launch_pack(const uint64_t* row_src, int n_rows_padded, int kd, int nkb, uint8_t* dst,
                        hipStream_t s);

@@ -206,6 +206,36 @@ dflash_status dflash_step(dflash_ctx *c, const void *feats, const int32_t *n_new
 dflash_status dflash_accept(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch,
                             int32_t K, int32_t *accept_len, void *stream);
 
+/* Loss-decay weighted cross-entropy for training the drafter (kongchang.com,
+ * "D-Flash", "Innovation 4: loss-decay weighted training": the CE of the
+ * token at in-block position k is weighted by gamma^k; "Innovation 3: random
+ * anchor sampling": block row k predicts the token k + 1 places after the
+ * block's clean anchor).  Rows are laid out as consecutive blocks of `block`
+ * rows, row r at in-block position r % block:
+ *   w_r  = gamma^(r % block) if 0 <= targets[r] < vocab, else 0
+ *   ce_r = logsumexp(logits_r) - logits_r[targets_r]      (0 if w_r = 0)
+ *   loss = sum_r w_r ce_r / sum_r w_r                      (0 if sum w = 0)
+ *   grad = d loss / d logits = w_r / sum w * (softmax(logits_r) - onehot)
+ * Arguments:
+ *   logits    dev [rows, vocab] of dtype, row-major, finite values
+ *   targets   dev [rows] int32; values outside [0, vocab) mark rows without
+ *             a token
+ *   rows      >= 0 (0 gives loss 0); vocab >= 1; block >= 1; gamma > 0
+ *   loss      dev [1] float out
+ *   ce        dev [rows] float out (may be NULL when rows = 0)
+ *   grad      dev [rows, vocab] of dtype out, or NULL for no gradient
+ *   workspace dev, DFLASH_DECAY_CE_WORKSPACE bytes, 8-byte aligned, owned by
+ *             the caller; calls that share it must be ordered on one stream
+ * Arithmetic in fp32 with fp64 sums over rows, in an order fixed by rows
+ * alone (the loss is reproducible bit for bit).  Logits are read once from
+ * HBM when rows are 16-byte aligned and vocab * element size is a multiple
+ * of 16 with at most 20480 16-byte vectors per row (bf16 vocab <= 163840,
+ * fp32 <= 81920), else twice.  Asynchronous on `stream`. */
+#define DFLASH_DECAY_CE_WORKSPACE 256
+dflash_status dflash_decay_ce(const void *logits, dflash_dtype dtype, const int32_t *targets,
+                              int32_t rows, int32_t vocab, int32_t block, double gamma, float *loss,
+                              float *ce, void *grad, void *workspace, void *stream);
+
 /* Host copies of the state: ctx_len and cap, host [batch] each (either may
  * be NULL). */
 dflash_status dflash_ctx_query(const dflash_ctx *c, int32_t *ctx_len, int32_t *cap);

@@ -295,3 +295,45 @@ def target_tokens(draft: np.ndarray, d: VerifierDraws, vocab: int) -> np.ndarray
     other = (draft + 1 + d.shift) % vocab
     return np.where(d.agree, draft, other).astype(np.int32)
 
+
+
+# --------------------------------------------------------------------------
+# drafter-training logits (loss-decay weighted cross-entropy)
+# --------------------------------------------------------------------------
+def ce_inputs(seed: int, rows: int, vocab: int, block: int, dtype: str, std: float = 2.0,
+              boost: Tuple[float, float] = (0.0, 12.0), cut_frac: float = 0.25,
+              masked_tail: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Logits [rows, vocab] and targets [rows] int32 of drafter blocks of
+    ``block`` rows (kongchang.com, "D-Flash", "Innovation 3: random anchor
+    sampling"; "Innovation 4: loss-decay weighted training").
+
+    Logits are N(0, std^2); the target's logit is then raised by a per-row
+    amount uniform in ``boost`` (rows range from confident to wrong).  A
+    fraction ``cut_frac`` of the blocks run past the end of their response:
+    their last u rows (u uniform in [1, block]) get the target -1.  The last
+    ``masked_tail`` vocabulary entries are -inf (padding of the vocabulary)
+    and never targets.  bf16 logits come back as raw bits (uint16)."""
+    L = normal(seed, "ce_logits", (rows, vocab), std, dtype)
+    g = stream(seed, "ce_targets")
+    live = vocab - masked_tail
+    t = g.integers(0, live, size=rows, dtype=np.int64)
+    up = g.uniform(boost[0], boost[1], size=rows).astype(np.float32)
+    nblk = (rows + block - 1) // block
+    cut = g.random(nblk) < cut_frac
+    ulen = g.integers(1, block + 1, size=nblk)
+    r = np.arange(rows)
+    if dtype == "bf16":
+        cur = (L[r, t].astype(np.uint32) << np.uint32(16)).view(np.float32)
+        L[r, t] = f32_to_bf16_bits(cur + up)
+        if masked_tail:
+            L[:, live:] = 0xFF80
+    else:
+        L[r, t] += up
+        if masked_tail:
+            L[:, live:] = -np.inf
+    pos = r % block
+    blk = r // block
+    blen = np.minimum(block, rows - blk * block)  # the last block may be short
+    dead = cut[blk] & (pos >= blen - ulen[blk])
+    t = np.where(dead, -1, t).astype(np.int32)
+    return L, t
