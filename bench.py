@@ -19,6 +19,7 @@ bounded sample of the same workload.
 
     python bench.py [--steps 50] [--warmup 10] [--workload 1]
     python bench.py --ksweep          # block-size sweep, one line per K
+    python bench.py --decay-ce        # drafter-training loss kernel instead
 """
 from __future__ import annotations
 
@@ -58,6 +59,10 @@ def parse():
                     help="report the single-launch block's per-phase timeline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--decay-ce", action="store_true",
+                    help="benchmark the loss-decay weighted cross-entropy (drafter training) instead")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the decay-CE oracle sample timed on the host")
     return ap.parse_args()
 
 
@@ -67,7 +72,15 @@ TRAFFIC = {
                 ["gemm_kernel.h", "gemm_argmax.hip", "gemm.hip", "kernels.h", "common.h"]),
     "persistent_draft": ("persistent_draft_qwen3_4b_k16_traffic.txt",
                          ["persist.hip", "kernels.h", "common.h"]),
+    "decay_ce": ("decay_ce_row_qwen_vocab_traffic.txt", ["loss.hip", "common.h"]),
 }
+
+# Loss-decay weighted CE workload: 256 drafter blocks of K = 16 rows over the
+# Qwen3 vocabulary (151936, of which the last 267 are padding at -inf), bf16
+# logits and gradient, gamma 0.8.
+CE_ROWS, CE_VOCAB, CE_BLOCK, CE_GAMMA, CE_MASKED, CE_SEED = 4096, 151936, 16, 0.8, 267, 2026
+CE_WORKLOAD = (f"decay-CE {CE_ROWS // CE_BLOCK} blocks x {CE_BLOCK} rows, vocab {CE_VOCAB} "
+               f"({CE_MASKED} masked), bf16, gamma {CE_GAMMA}")
 
 
 def kernel_source_hash(kernel: str):
@@ -227,6 +240,81 @@ def cpu_baseline(wl, K, w, n_steps):
                       f"'{wl.name}' after an untimed prefill and one untimed step; {dt:.2f} s/step"}
 
 
+def decay_ce_cpu_baseline(L, t, n_rows):
+    """The fp64 oracle on the first n_rows rows (whole blocks) of the decay-CE
+    workload, loss and gradient."""
+    from oracle import dflash as O
+    from oracle import loss as OL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n_rows = max(CE_BLOCK, n_rows // CE_BLOCK * CE_BLOCK)
+    Lf = O.to_f64(L[:n_rows], "bf16")
+    t0 = time.time()
+    OL.decay_ce(Lf, t[:n_rows], CE_BLOCK, CE_GAMMA, want_grad=True)
+    dt = time.time() - t0
+    return {"value": round(n_rows / dt, 2), "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"loss and gradient of the first {n_rows} rows ({n_rows // CE_BLOCK} blocks) of the "
+                      f"same logits in fp64 (bf16 to fp64 conversion untimed); {dt:.2f} s"}
+
+
+def bench_decay_ce(args, torch, dfl):
+    """Loss-decay weighted CE + gradient of one batch of drafter logits per
+    step (three launches: weight sum and row scales, rows, loss)."""
+    import synth
+    log(f"[bench] decay-CE inputs: {CE_WORKLOAD}")
+    L, t = synth.ce_inputs(CE_SEED, CE_ROWS, CE_VOCAB, CE_BLOCK, "bf16", masked_tail=CE_MASKED)
+    d_L = torch.from_numpy(L.view(np.int16)).view(torch.bfloat16).cuda()
+    d_t = torch.from_numpy(t).cuda()
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    ce = torch.empty(CE_ROWS, dtype=torch.float32, device="cuda")
+    grad = torch.empty_like(d_L)
+    ws = torch.empty(dfl.DECAY_CE_WORKSPACE, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dfl.dflash_decay_ce(d_L, d_t, CE_BLOCK, CE_GAMMA, loss, ce, grad, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = e0.elapsed_time(e1) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    bytes_per_call = 2 * CE_ROWS * CE_VOCAB * 2   # one read of the logits, one write of the gradient
+    achieved = bytes_per_call / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": "loss-decay weighted CE + gradient over drafter logits (rows/s); % HBM peak",
+        "value": round(CE_ROWS / (wall / args.steps), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": CE_WORKLOAD, "rows": CE_ROWS, "vocab": CE_VOCAB, "block": CE_BLOCK,
+                   "gamma": CE_GAMMA, "parallelism": "1 GPU"},
+        "loss": round(float(loss.item()), 6),
+        "roofline": {"kernel": "dflash_decay_ce call (ce_scale, ce_row_kernel<bf16, 19>, ce_loss launches)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decay_ce", CE_WORKLOAD, CE_BLOCK),
+                     "avg_launch_ms": round(call_ms, 5), "launches": args.steps,
+                     "bytes_per_launch": int(bytes_per_call)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = decay_ce_cpu_baseline(L, t, args.cpu_rows)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -238,6 +326,11 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.decay_ce:
+        if args.copy_calibration:
+            copy_calibration(torch)
+        bench_decay_ce(args, torch, dfl)
+        return
     if args.copy_calibration:
         copy_calibration(torch)
     wl = synth.workload(3 if args.ksweep else args.workload)
