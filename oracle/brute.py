@@ -149,3 +149,80 @@ def forward(shape, weights: Dict, feats, ids: Sequence[int],
         L.append(lg)
         D.append(best)
     return D, L, Z
+
+
+def target_forward(shape, weights: Dict, ids: Sequence[int],
+                   taps: Sequence[int] = ()) -> Tuple[List[int], List[List[float]], List[List[float]]]:
+    """Causal forward of a whole sequence from an empty cache (the target of
+    block verification; Google Developers Blog, "Overcoming the
+    autoregressive bottleneck"): position i attends to positions 0..i.
+
+    Returns (argmax per position, logits rows, tapped residual rows: the
+    residual after each layer in ``taps``, concatenated in tap order).
+    """
+    s = shape
+    dt = s.dtype
+    H, d = s.hidden, s.head_dim
+    nq, nkv = s.n_q_heads, s.n_kv_heads
+    E = _val(weights["embed"], dt)
+    n = len(ids)
+    X = [list(E[int(t)]) for t in ids]
+    T = [[] for _ in range(n)]
+    for l in range(s.n_layers):
+        p = f"layers.{l}."
+        g1 = _val(weights[p + "attn_norm"], dt)
+        Wq, Wk, Wv = (_val(weights[p + nm], dt) for nm in ("wq", "wk", "wv"))
+        Wo = _val(weights[p + "wo"], dt)
+        Q, Kr, Vr = [], [], []
+        for i in range(n):
+            u = _rmsnorm(X[i], g1, s.rms_eps)
+            qf, kf, vf = _matvec(Wq, u), _matvec(Wk, u), _matvec(Wv, u)
+            Q.append([_rope_head(qf[h * d:(h + 1) * d], i, s.rope_theta) for h in range(nq)])
+            Kr.append([_rope_head(kf[g * d:(g + 1) * d], i, s.rope_theta) for g in range(nkv)])
+            Vr.append([vf[g * d:(g + 1) * d] for g in range(nkv)])
+        group = nq // nkv
+        newX = []
+        for i in range(n):
+            o = []
+            for h in range(nq):
+                g = h // group
+                sc = []
+                for j in range(i + 1):            # causal: keys 0..i only
+                    dot = 0.0
+                    for c in range(d):
+                        dot += Q[i][h][c] * Kr[j][g][c]
+                    sc.append(dot / math.sqrt(d))
+                mx = max(sc)
+                e = [math.exp(v - mx) for v in sc]
+                tot = sum(e)
+                for c in range(d):
+                    acc = 0.0
+                    for j in range(i + 1):
+                        acc += e[j] / tot * Vr[j][g][c]
+                    o.append(acc)
+            att = _matvec(Wo, o)
+            newX.append([X[i][c] + att[c] for c in range(H)])
+        X = newX
+        g2 = _val(weights[p + "mlp_norm"], dt)
+        Wg, Wu, Wd = (_val(weights[p + nm], dt) for nm in ("w_gate", "w_up", "w_down"))
+        for i in range(n):
+            w = _rmsnorm(X[i], g2, s.rms_eps)
+            gt, up = _matvec(Wg, w), _matvec(Wu, w)
+            act = [gt[c] / (1.0 + math.exp(-gt[c])) * up[c] for c in range(len(gt))]
+            dn = _matvec(Wd, act)
+            X[i] = [X[i][c] + dn[c] for c in range(H)]
+        if l in taps:
+            for i in range(n):
+                T[i] = T[i] + list(X[i])
+    gf = _val(weights["final_norm"], dt)
+    Wlm = _val(weights["lm_head"], dt)
+    L, D = [], []
+    for i in range(n):
+        lg = _matvec(Wlm, _rmsnorm(X[i], gf, s.rms_eps))
+        best = 0
+        for v in range(1, len(lg)):
+            if lg[v] > lg[best]:
+                best = v
+        L.append(lg)
+        D.append(best)
+    return D, L, T
