@@ -13,6 +13,8 @@ Entry points keep the C names:
   dflash_draft_block               (a4)-(a9) one non-causal draft forward
   dflash_accept                    (a10) greedy acceptance
   dflash_decay_ce                  loss-decay weighted cross-entropy (training)
+  dflash_target_create / Model(target=True), dflash_verify_block,
+  dflash_commit                    target-side block verification
 """
 from __future__ import annotations
 
@@ -67,7 +69,8 @@ class _Allocator(ctypes.Structure):
 EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_model_create",
            "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
            "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_step",
-           "dflash_accept", "dflash_decay_ce",
+           "dflash_accept", "dflash_decay_ce", "dflash_target_create", "dflash_verify_block",
+           "dflash_commit",
            "dflash_ctx_query", "dflash_ctx_buffers", "dflash_ctx_set_persistent",
            "dflash_ctx_persistent_path", "dflash_ctx_check", "dflash_persist_trace",
            "dflash_profile_enable",
@@ -99,6 +102,10 @@ def _load() -> ctypes.CDLL:
         "dflash_accept": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
         "dflash_decay_ce": ([vp, ctypes.c_int, vp, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp, vp],
                             ctypes.c_int),
+        "dflash_target_create": ([ctypes.POINTER(_Config), ctypes.POINTER(_Weights), i32p,
+                                  ctypes.POINTER(_Allocator), vp, ctypes.POINTER(vp)], ctypes.c_int),
+        "dflash_verify_block": ([vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
+        "dflash_commit": ([vp, i32p, vp], ctypes.c_int),
         "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
         "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                 ctypes.POINTER(vp), i32p], ctypes.c_int),
@@ -188,17 +195,21 @@ def config_struct(shape) -> _Config:
 
 
 class Model:
-    """dflash_model_create / dflash_model_destroy.
+    """dflash_model_create / dflash_model_destroy (a drafter), or with
+    ``taps`` given, dflash_target_create (a verification target whose
+    ``shape.n_feat`` equals ``len(taps)``).
 
-    ``weights``: device tensors keyed ``embed``, ``lm_head``, ``fc``,
-    ``final_norm`` and ``layers.{l}.{attn_norm,wq,wk,wv,wo,mlp_norm,w_gate,
-    w_up,w_down}`` in the model dtype (bf16 may be given as uint16 bits).
-    ``embed`` stays borrowed: this object keeps a reference to it.
+    ``weights``: device tensors keyed ``embed``, ``lm_head``, ``fc`` (drafter
+    only), ``final_norm`` and ``layers.{l}.{attn_norm,wq,wk,wv,wo,mlp_norm,
+    w_gate,w_up,w_down}`` in the model dtype (bf16 may be given as uint16
+    bits).  ``embed`` stays borrowed: this object keeps a reference to it.
     """
 
     def __init__(self, shape, weights: Dict[str, torch.Tensor], device="cuda",
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, taps: Optional[Sequence[int]] = None):
         self.shape = shape
+        self.target = taps is not None
+        self.taps = list(taps) if taps is not None else []
         self.device = torch.device(device)
         self.alloc = TorchAllocator(self.device)
         self._embed = weights["embed"]
@@ -208,14 +219,23 @@ class Model:
         for l in range(L):
             for k in keys:
                 setattr(layers[l], k, _ptr(weights[f"layers.{l}.{k}"]))
-        w = _Weights(_ptr(weights["embed"]), _ptr(weights["lm_head"]), _ptr(weights["fc"]),
-                     _ptr(weights["final_norm"]), layers)
+        w = _Weights(_ptr(weights["embed"]), _ptr(weights["lm_head"]),
+                     None if self.target else _ptr(weights["fc"]), _ptr(weights["final_norm"]), layers)
         cfg = config_struct(shape)
         h = ctypes.c_void_p()
-        _check("dflash_model_create",
-               lib.dflash_model_create(ctypes.byref(cfg), ctypes.byref(w),
-                                       ctypes.byref(self.alloc.struct), _stream(stream),
-                                       ctypes.byref(h)))
+        if self.target:
+            if len(self.taps) != shape.n_feat:
+                raise ValueError("a target's shape.n_feat must equal len(taps)")
+            tp = (ctypes.c_int32 * max(len(self.taps), 1))(*[int(t) for t in self.taps])
+            _check("dflash_target_create",
+                   lib.dflash_target_create(ctypes.byref(cfg), ctypes.byref(w), tp,
+                                            ctypes.byref(self.alloc.struct), _stream(stream),
+                                            ctypes.byref(h)))
+        else:
+            _check("dflash_model_create",
+                   lib.dflash_model_create(ctypes.byref(cfg), ctypes.byref(w),
+                                           ctypes.byref(self.alloc.struct), _stream(stream),
+                                           ctypes.byref(h)))
         self.handle = h
 
     def bytes(self):
@@ -420,6 +440,33 @@ def dflash_decay_ce(logits: torch.Tensor, targets: torch.Tensor, block: int, gam
            lib.dflash_decay_ce(_ptr(logits), dt, _ptr(targets), int(rows), int(vocab), int(block),
                                float(gamma), _ptr(loss), _ptr(ce), _ptr(grad), _ptr(workspace),
                                _stream(stream)))
+
+
+def dflash_verify_block(ctx: Context, block_ids: torch.Tensor, K1: int, target_ids: torch.Tensor,
+                        logits: Optional[torch.Tensor] = None, taps: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None) -> None:
+    """One causal target forward over blocks [B, K1] (the anchor and K1 - 1
+    drafts): target_ids [B, K1] int32 out (the target's token for the
+    position after each row), optional float32 logits [B, K1, V] and taps
+    [B, K1, n_taps * H] in the model dtype."""
+    for t in (block_ids, target_ids):
+        if t.dtype != torch.int32 or t.numel() != ctx.batch * K1:
+            raise ValueError("block_ids / target_ids must be int32 [batch, K1]")
+    sh = ctx.model.shape
+    if logits is not None and (logits.dtype != torch.float32 or logits.numel() != ctx.batch * K1 * sh.vocab):
+        raise ValueError("logits must be float32 [batch, K1, vocab]")
+    if taps is not None and taps.numel() != ctx.batch * K1 * len(ctx.model.taps) * sh.hidden:
+        raise ValueError("taps must be [batch, K1, n_taps * hidden]")
+    _check("dflash_verify_block",
+           lib.dflash_verify_block(ctx.handle, _ptr(block_ids), int(K1), _ptr(target_ids), _ptr(logits),
+                                   _ptr(taps), _stream(stream)))
+
+
+def dflash_commit(ctx: Context, n_acc: Sequence[int], stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Keep the first n_acc[b] rows of the last verified block in sequence
+    b's cache (host counts)."""
+    nn = (ctypes.c_int32 * ctx.batch)(*[int(n) for n in n_acc])
+    _check("dflash_commit", lib.dflash_commit(ctx.handle, nn, _stream(stream)))
 
 
 def version() -> str:

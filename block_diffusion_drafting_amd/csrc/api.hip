@@ -85,6 +85,10 @@ struct dflash_model {
   Packed lm, fc, kv;
   PLayer* players = nullptr;   // device [L]: the layer table of the persistent draft kernel
   int64_t layer_bytes = 0, lm_bytes = 0, proj_bytes = 0;
+  // a verification target (dflash_target_create): causal, no context
+  // projection; tapped layers in increasing order (cfg.n_feat of them)
+  bool target = false;
+  std::vector<int> taps;
 
   const float* attn_gain(int l) const { return gains + (size_t)(2 * l) * cfg.hidden; }
   const float* mlp_gain(int l) const { return gains + (size_t)(2 * l + 1) * cfg.hidden; }
@@ -126,6 +130,7 @@ struct dflash_ctx {
   const dflash_model* m = nullptr;
   Profiler prof;
   int B = 0;
+  int verified = 0;   // target contexts: rows of the last verified block (0 after a commit)
   Alloc alloc;
   std::vector<DevSeq> seq;  // host mirror (ctx_len, cap, phys, pointers)
   DevSeq* seq_dev = nullptr;
@@ -208,7 +213,7 @@ struct PhaseTimer {
   }
 };
 
-dflash_status check_config(const dflash_config* c) {
+dflash_status check_config(const dflash_config* c, bool target = false) {
   if (!c) return fail(DFLASH_E_ARG, "config is NULL");
   if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "bad dtype %d", (int)c->dtype);
   if (c->hidden <= 0 || c->hidden % 64) return fail(DFLASH_E_SHAPE, "hidden %d must be a positive multiple of 64", c->hidden);
@@ -218,7 +223,8 @@ dflash_status check_config(const dflash_config* c) {
     return fail(DFLASH_E_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
   if (c->intermediate <= 0 || c->intermediate % 8) return fail(DFLASH_E_SHAPE, "intermediate %d must be a positive multiple of 8", c->intermediate);
   if (c->vocab <= 0) return fail(DFLASH_E_SHAPE, "vocab %d", c->vocab);
-  if (c->n_feat <= 0 || (int64_t)c->n_feat * c->hidden > (1 << 24)) return fail(DFLASH_E_SHAPE, "n_feat %d", c->n_feat);
+  if (c->n_feat < (target ? 0 : 1) || (int64_t)c->n_feat * c->hidden > (1 << 24))
+    return fail(DFLASH_E_SHAPE, "n_feat %d", c->n_feat);
   if (!(c->rope_theta > 1.0) || !(c->rms_eps >= 0.0)) return fail(DFLASH_E_ARG, "rope_theta must be > 1 and rms_eps >= 0");
   return DFLASH_OK;
 }
@@ -269,8 +275,8 @@ void plain_rows(std::vector<uint64_t>& rows, const uint8_t* w, int n, int row_by
   for (int r = 0; r < n; ++r) rows.push_back((uint64_t)(w + (size_t)r * row_bytes));
 }
 
-bool valid_stream_ptrs(const dflash_weights* w, int L) {
-  if (!w || !w->embed || !w->lm_head || !w->fc || !w->final_norm) return false;
+bool valid_stream_ptrs(const dflash_weights* w, int L, bool target = false) {
+  if (!w || !w->embed || !w->lm_head || (!target && !w->fc) || !w->final_norm) return false;
   if (L > 0 && !w->layers) return false;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& lw = w->layers[l];
@@ -289,17 +295,27 @@ const char* dflash_version(void) { return "dflash-mi355x 0.1 (gfx950)"; }
 int32_t dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
 const char* dflash_last_error(void) { return g_err.c_str(); }
 
-dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
-                                  const dflash_allocator* alloc, void* stream, dflash_model** out) {
+}  // extern "C"
+
+static dflash_status model_create(const dflash_config* cfg, const dflash_weights* w, const int32_t* taps,
+                                  bool target, const dflash_allocator* alloc, void* stream, dflash_model** out) {
   if (!out) return fail(DFLASH_E_ARG, "out is NULL");
   *out = nullptr;
-  dflash_status st = check_config(cfg);
+  dflash_status st = check_config(cfg, target);
   if (st) return st;
-  if (!valid_stream_ptrs(w, cfg->n_layers)) return fail(DFLASH_E_ARG, "a weight pointer is NULL");
+  if (!valid_stream_ptrs(w, cfg->n_layers, target)) return fail(DFLASH_E_ARG, "a weight pointer is NULL");
   if (alloc && (!alloc->alloc || !alloc->free)) return fail(DFLASH_E_ARG, "allocator callbacks are NULL");
+  if (target) {
+    if (cfg->n_feat > 0 && !taps) return fail(DFLASH_E_ARG, "taps is NULL");
+    for (int i = 0; i < cfg->n_feat; ++i)
+      if (taps[i] < 0 || taps[i] >= cfg->n_layers || (i > 0 && taps[i] <= taps[i - 1]))
+        return fail(DFLASH_E_ARG, "taps must be increasing layer indices in [0, %d)", cfg->n_layers);
+  }
   hipStream_t s = (hipStream_t)stream;
   dflash_model* m = new dflash_model();
   m->cfg = *cfg;
+  m->target = target;
+  if (target) m->taps.assign(taps, taps + cfg->n_feat);
   m->es = cfg->dtype == DFLASH_BF16 ? 2 : 4;
   m->ces = m->es;
   if (alloc) {
@@ -373,6 +389,9 @@ dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights
     if ((st = pack(m, rows, H, s, m->lm))) return cleanup(st);
     m->lm_bytes = packed_bytes(m->lm);
     rows.clear();
+  }
+  if (!target) {
+    std::vector<uint64_t> rows;
     plain_rows(rows, (const uint8_t*)w->fc, H, cfg->n_feat * H * es);
     if ((st = pack(m, rows, cfg->n_feat * H, s, m->fc))) return cleanup(st);
     rows.clear();
@@ -385,7 +404,7 @@ dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights
     }
     m->proj_bytes = packed_bytes(m->fc) + (L > 0 ? packed_bytes(m->kv) : 0);
   }
-  if (L > 0) {
+  if (L > 0 && !target) {
     std::vector<PLayer> tbl(L);
     for (int l = 0; l < L; ++l) {
       tbl[l].qkv = m->qkv[l];
@@ -404,6 +423,18 @@ dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights
   }
   *out = m;
   return DFLASH_OK;
+}
+
+extern "C" {
+
+dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
+                                  const dflash_allocator* alloc, void* stream, dflash_model** out) {
+  return model_create(cfg, w, nullptr, false, alloc, stream, out);
+}
+
+dflash_status dflash_target_create(const dflash_config* cfg, const dflash_weights* w, const int32_t* taps,
+                                   const dflash_allocator* alloc, void* stream, dflash_model** out) {
+  return model_create(cfg, w, taps, true, alloc, stream, out);
 }
 
 dflash_status dflash_model_destroy(dflash_model* m) {
@@ -433,10 +464,10 @@ static dflash_status alloc_seq(dflash_ctx* c, int b, int cap, DevSeq& out) {
   v.ctx_len = c->seq[b].ctx_len;
   v.cap = cap;
   v.phys = phys;
-  v.ctxbuf = c->alloc.get((size_t)phys * m->cfg.hidden * sizeof(float));
+  v.ctxbuf = m->target ? nullptr : c->alloc.get((size_t)phys * m->cfg.hidden * sizeof(float));
   v.k = c->alloc.get(kvn * ces);
   v.vt = c->alloc.get(kvn * ces);
-  if (!v.ctxbuf || !v.k || !v.vt) {
+  if ((!m->target && !v.ctxbuf) || !v.k || !v.vt) {
     c->alloc.put(v.ctxbuf);
     c->alloc.put(v.k);
     c->alloc.put(v.vt);
@@ -616,7 +647,7 @@ static dflash_status grow_for(dflash_ctx* c, const int32_t* n_new, hipStream_t s
     DevSeq nv;
     dflash_status st = alloc_seq(c, b, cap, nv);
     if (st) return st;
-    if (v.ctxbuf) {
+    if (v.k) {
       PhaseTimer tm(c, PH_GROW, s);
       hipError_t e = launch_grow_copy<typename CacheOf<T>::type>(v, nv, m->cfg.n_layers, m->cfg.n_kv_heads,
                                                                 m->cfg.head_dim, H, s);
@@ -687,6 +718,7 @@ extern "C" {
 dflash_status dflash_project_ctx(dflash_ctx* c, const void* feats, const int32_t* n_new,
                                  const int32_t* positions, void* stream) {
   if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (c->m->target) return fail(DFLASH_E_STATE, "a target context verifies blocks (dflash_verify_block)");
   if (!n_new) return fail(DFLASH_E_ARG, "n_new is NULL");
   int64_t total = 0;
   for (int b = 0; b < c->B; ++b) {
@@ -883,11 +915,19 @@ struct FusedCtx {
   Frag x{};
 };
 
+// Block verification by a target model: the same layer sequence, causal,
+// the block rows' K/V written to the cache, tapped hidden states copied out.
+struct VerifyOpts {
+  bool on = false;
+  void* taps = nullptr;   // [M][n_taps*H] model type, or null
+};
+
 template <typename T>
 static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_t* draft, float* logits,
-                                void* hidden, hipStream_t s, const FusedCtx& fused = FusedCtx{}) {
+                                void* hidden, hipStream_t s, const FusedCtx& fused = FusedCtx{},
+                                const VerifyOpts& vo = VerifyOpts{}) {
   using CT = typename CacheOf<T>::type;
-  if (fused.n_ctx == 0 && persist_ok(c, K)) return persist_draft(c, ids, K, draft, logits, hidden, s);
+  if (!vo.on && fused.n_ctx == 0 && persist_ok(c, K)) return persist_draft(c, ids, K, draft, logits, hidden, s);
   const dflash_model* m = c->m;
   const dflash_config& cf = m->cfg;
   const int B = c->B, M = B * K, H = cf.hidden, L = cf.n_layers, d = cf.head_dim;
@@ -919,14 +959,16 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   const int qg_per_wg = qgroups > 1 ? 2 : 1;
   const int64_t wg_per_split = (int64_t)nkv * ((qgroups + qg_per_wg - 1) / qg_per_wg);
   const int64_t round_wgs = (qg_per_wg == 1 ? 2 : 1) * (int64_t)c->attn_wgs_per_cu * 256;
+  auto splits = [&](int len, int ch) {
+    return vo.on ? (len + K + ch - 1) / ch : (len + ch - 1) / ch + (K + ch - 1) / ch;
+  };
   int chunk = 128;
   for (;; chunk += 64) {
     int64_t wgs = 0;
-    for (int b = 0; b < B; ++b)
-      wgs += wg_per_split * ((c->seq[b].ctx_len + chunk - 1) / chunk + (K + chunk - 1) / chunk);
+    for (int b = 0; b < B; ++b) wgs += wg_per_split * splits(c->seq[b].ctx_len, chunk);
     if (wgs <= round_wgs || chunk >= max_len + K) break;
   }
-  const int max_splits = (max_len + chunk - 1) / chunk + (K + chunk - 1) / chunk;
+  const int max_splits = splits(max_len, chunk);
   if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d) * sizeof(float))))
     return st;
 
@@ -964,6 +1006,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   a.chunk = chunk;
   a.max_splits = max_splits;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  a.causal = vo.on ? 1 : 0;
 
   const Frag none{};
   for (int l = 0; l < L; ++l) {
@@ -978,6 +1021,11 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
       if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], fused.x, nullptr, 0, fused.mt0 * 16 + fused.n_ctx, ef,
                             s, nullptr, true)))
         return st;
+    } else if (vo.on) {
+      EpiArgs ev = e;   // the block rows' K/V go to layer l of the cache
+      ev.kv_cache = 1;
+      ev.layer = l;
+      if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], xg, nullptr, 0, M, ev, s))) return st;
     } else if ((st = run_gemm<T>(c, PH_QKV, EPI_QKV, m->qkv[l], xg, nullptr, 0, M, e, s))) {
       return st;
     }
@@ -1023,6 +1071,11 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
       HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
                                    l + 1 < L ? m->attn_gain(l + 1) : m->final_gain(), xg, (float*)c->ssq.p, s,
                                    wn));
+      if (vo.on && vo.taps) {
+        const int nt = (int)m->taps.size();
+        for (int ti = 0; ti < nt; ++ti)
+          if (m->taps[ti] == l) HIP_TRY(launch_tap<T>((const float*)c->x.p, M, H, ti, nt, vo.taps, s));
+      }
     }
   }
   (void)none;
@@ -1082,6 +1135,7 @@ extern "C" {
 dflash_status dflash_step(dflash_ctx* c, const void* feats, const int32_t* n_new, const int32_t* block_ids,
                           int32_t K, int32_t* draft_ids, float* logits, void* hidden, void* stream) {
   if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (c->m->target) return fail(DFLASH_E_STATE, "a target context verifies blocks (dflash_verify_block)");
   if (!n_new) return fail(DFLASH_E_ARG, "n_new is NULL");
   if (!block_ids || !draft_ids) return fail(DFLASH_E_ARG, "block_ids / draft_ids is NULL");
   if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
@@ -1103,11 +1157,57 @@ dflash_status dflash_step(dflash_ctx* c, const void* feats, const int32_t* n_new
 dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* block_ids, int32_t K, int32_t* draft_ids,
                                  float* logits, void* hidden, void* stream) {
   if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (c->m->target) return fail(DFLASH_E_STATE, "a target context verifies blocks (dflash_verify_block)");
   if (!block_ids || !draft_ids) return fail(DFLASH_E_ARG, "block_ids / draft_ids is NULL");
   if (K < 1 || K > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K = %d out of [1, %d]", K, DFLASH_MAX_K);
   hipStream_t s = (hipStream_t)stream;
   return c->m->cfg.dtype == DFLASH_BF16 ? draft_impl<bf16_t>(c, block_ids, K, draft_ids, logits, hidden, s)
                                         : draft_impl<float>(c, block_ids, K, draft_ids, logits, hidden, s);
+}
+
+dflash_status dflash_verify_block(dflash_ctx* c, const int32_t* block_ids, int32_t K1, int32_t* target_ids,
+                                  float* logits, void* taps, void* stream) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!c->m->target) return fail(DFLASH_E_STATE, "not a target context (dflash_target_create)");
+  if (!block_ids || !target_ids) return fail(DFLASH_E_ARG, "block_ids / target_ids is NULL");
+  if (K1 < 1 || K1 > DFLASH_MAX_K) return fail(DFLASH_E_ARG, "K1 = %d out of [1, %d]", K1, DFLASH_MAX_K);
+  if (taps && c->m->taps.empty()) return fail(DFLASH_E_ARG, "taps requested from a model without tapped layers");
+  std::vector<int32_t> n(c->B, K1);
+  for (int b = 0; b < c->B; ++b)
+    if ((int64_t)c->seq[b].ctx_len + K1 > (1 << 30))
+      return fail(DFLASH_E_SHAPE, "sequence %d would exceed 2^30 positions", b);
+  hipStream_t s = (hipStream_t)stream;
+  VerifyOpts vo;
+  vo.on = true;
+  vo.taps = taps;
+  dflash_status st;
+  // room for the block's K/V at slots ctx_len .. ctx_len + K1 - 1
+  if (c->m->cfg.dtype == DFLASH_BF16) {
+    if ((st = grow_for<bf16_t>(c, n.data(), s))) return st;
+    st = draft_impl<bf16_t>(c, block_ids, K1, target_ids, logits, nullptr, s, FusedCtx{}, vo);
+  } else {
+    if ((st = grow_for<float>(c, n.data(), s))) return st;
+    st = draft_impl<float>(c, block_ids, K1, target_ids, logits, nullptr, s, FusedCtx{}, vo);
+  }
+  c->verified = st == DFLASH_OK ? K1 : 0;
+  return st;
+}
+
+dflash_status dflash_commit(dflash_ctx* c, const int32_t* n_acc, void* stream) {
+  if (!c) return fail(DFLASH_E_ARG, "ctx is NULL");
+  if (!c->m->target) return fail(DFLASH_E_STATE, "not a target context (dflash_target_create)");
+  if (!n_acc) return fail(DFLASH_E_ARG, "n_acc is NULL");
+  for (int b = 0; b < c->B; ++b)
+    if (n_acc[b] < 0 || n_acc[b] > c->verified)
+      return fail(DFLASH_E_STATE, "n_acc[%d] = %d: the last verified block has %d rows", b, n_acc[b], c->verified);
+  hipStream_t s = (hipStream_t)stream;
+  for (int b = 0; b < c->B; ++b) {
+    if (n_acc[b] == 0) continue;
+    c->seq[b].ctx_len += n_acc[b];
+    HIP_TRY(launch_set_seq(c->seq_dev, b, c->seq[b], s));
+  }
+  c->verified = 0;
+  return DFLASH_OK;
 }
 
 dflash_status dflash_ctx_set_persistent(dflash_ctx* c, int32_t enable) {

@@ -1,4 +1,5 @@
-// Bidirectional GQA attention of the draft block over [context KV || block KV].
+// Bidirectional GQA attention of the draft block over [context KV || block KV]
+// (and, in its causal form, the target's attention for block verification).
 //
 // The block is denoised in one non-causal forward (kongchang.com "D-Flash",
 // "System architecture"; Google Developers Blog, "Dual cache for
@@ -18,6 +19,11 @@
 // the scale).  For bf16 the two 16-key S^T tiles of a 32-key step hold keys
 // in the order that makes each lane's probabilities the B-fragment of the
 // P.V product directly.
+//
+// Causal form (block verification, Google Developers Blog "Overcoming the
+// autoregressive bottleneck"): the QKV product has already stored the block
+// rows' K/V in the cache at slots ctx_len + i, so every split reads the
+// cache, over ctx_len + K keys, and block row i masks keys past ctx_len + i.
 //
 // T is the attention operand type: fp16 for bf16 models (queries, keys,
 // values and probabilities), fp32 for fp32 models.  The output is fp32.
@@ -84,9 +90,8 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
 
   const DevSeq sq = a.seqs[b];
   const int ctx_len = sq.ctx_len;
-  const int n_cs = (ctx_len + a.chunk - 1) / a.chunk;
-  const int n_bs = (a.K + a.chunk - 1) / a.chunk;
-  const int n_s = n_cs + n_bs;
+  int n_cs, n_s;
+  attn_split_counts(a, ctx_len, n_cs, n_s);
   if (s >= n_s) return;
 
   const T* kbase;
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
     vbase = (const T*)sq.vt + ((size_t)a.layer * a.nkv + g) * D * sq.phys;
     vstride = sq.phys;
     k0 = s * a.chunk;
-    k1 = min(ctx_len, k0 + a.chunk);
+    k1 = min(a.causal ? ctx_len + a.K : ctx_len, k0 + a.chunk);
   } else {
     kbase = (const T*)a.bk + ((size_t)b * a.nkv + g) * a.Kpad * D;
     vbase = (const T*)a.bvt + ((size_t)b * a.nkv + g) * D * a.Kpad;
@@ -114,6 +119,8 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
   const bool row_ok = qg < a.qgroups && r < nrows;
   const int h = g * rep + (row_ok ? r / a.K : 0);
   const int i = row_ok ? r % a.K : 0;
+  // causal form: this lane's query (block row i) sees cache keys 0..ctx_len+i
+  const int key_lim = a.causal ? ctx_len + i : 0x7FFFFFFF;
   u32x4 qf[NFD];
   {
     const T* qp = (const T*)a.q + ((size_t)(b * a.K + i) * a.nq + h) * D;
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int j = 0; j < 8; ++j) {
         if (j < nv) {
           const int key = c0 + kb + g4 * nv + j;
-          sv[j] = (key < cend) ? sv[j] * a.scale_log2 : -INFINITY;
+          sv[j] = (key < cend && key <= key_lim) ? sv[j] * a.scale_log2 : -INFINITY;
           mx = fmaxf(mx, sv[j]);
         }
       }
@@ -322,7 +329,8 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out
   const int g = u % a.nkv;
   const int b = u / a.nkv;
   const int ctx_len = a.seqs[b].ctx_len;
-  const int n_s = (ctx_len + a.chunk - 1) / a.chunk + (a.K + a.chunk - 1) / a.chunk;
+  int n_cs, n_s;
+  attn_split_counts(a, ctx_len, n_cs, n_s);
   const int per = (n_s + 3) / 4;
   const int s_begin = min(n_s, quarter * per), s_end = min(n_s, s_begin + per);
   const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;

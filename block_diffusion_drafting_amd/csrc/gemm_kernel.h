@@ -130,6 +130,12 @@ __device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 a
     for (int j = 0; j < 4; ++j) y[j] = acc[j] * r;
     const int b = m / e.Kblk, i = m - b * e.Kblk;
     const int pos = e.seqs[b].ctx_len + i;
+    if (e.kv_cache && n >= qd) {
+      // verified block: K/V straight into the cache at slot = position
+      const RowMap rm{b, pos, pos, 0};
+      store_ctx_kv<CT>(e, e.layer, n - qd, rm, f32x4{y[0], y[1], y[2], y[3]}, g4);
+      return;
+    }
     if (n < qd + kvd) {
       const bool isq = n < qd;
       const int nn = isq ? n : n - qd;

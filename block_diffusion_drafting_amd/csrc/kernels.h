@@ -76,6 +76,9 @@ struct EpiArgs {
   // fused step: context rows appended to the QKV activations from m-tile
   // ctx_mt0 on; their K/V go to layer `layer` of the caches
   int32_t ctx_mt0, n_ctx, layer;
+  // block verification (EPI_QKV): the block rows' K/V go to layer `layer`
+  // of the caches at slot = position = ctx_len + i instead of bk / bvt
+  int32_t kv_cache;
   // EPI_RESNORM: residual x [M][H] (fp32), gain of the next norm, its frag
   // output and sums of squares [H/16][M]
   float* xres;
@@ -167,7 +170,21 @@ struct AttnArgs {
   int32_t B, K, Kpad, nq, nkv, d, layer;
   int32_t qgroups, chunk, max_splits;
   float scale_log2;
+  // block verification: every key comes from the cache (the block's were
+  // stored there by the QKV product), block row i sees keys 0..ctx_len+i
+  int32_t causal;
 };
+// Splits of one (sequence, KV head): context keys, then block keys (or, in
+// the causal form, ctx_len + K cache keys).
+__host__ __device__ inline void attn_split_counts(const AttnArgs& a, int ctx_len, int& n_cs, int& n_s) {
+  if (a.causal) {
+    n_cs = (ctx_len + a.K + a.chunk - 1) / a.chunk;
+    n_s = n_cs;
+  } else {
+    n_cs = (ctx_len + a.chunk - 1) / a.chunk;
+    n_s = n_cs + (a.K + a.chunk - 1) / a.chunk;
+  }
+}
 size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d);
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
@@ -198,6 +215,10 @@ template <typename T>
 hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri, int B,
                               const int32_t* positions, RowMap* rowmap, DevSeq* seqs, Frag cbuf,
                               int row0, hipStream_t s);
+// out[m][tap*H + h] = x[m][h] in the model type (a tapped hidden state;
+// out rows are n_taps*H long).
+template <typename T>
+hipError_t launch_tap(const float* x, int M, int H, int tap, int n_taps, void* out, hipStream_t s);
 // draft ids from argmax keys; optional final-normed hidden rows.
 template <typename T>
 hipError_t launch_finalize(const unsigned long long* keys, int M, int32_t* draft, const float* x,

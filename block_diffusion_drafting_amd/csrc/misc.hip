@@ -343,7 +343,7 @@ hipError_t launch_set_seq(DevSeq* seqs, int b, DevSeq v, hipStream_t s) {
 template <typename T>
 __global__ void grow_copy_kernel(DevSeq o, DevSeq n, int L, int nkv, int d, int H) {
   const int len = o.ctx_len;
-  const size_t n_ctx = (size_t)len * H;
+  const size_t n_ctx = o.ctxbuf ? (size_t)len * H : 0;   // a target's sequences have no feature buffer
   const size_t n_k = (size_t)L * nkv * len * d;
   const size_t n_v = (size_t)L * nkv * d * len;
   const size_t total = n_ctx + n_k + n_v;
@@ -379,6 +379,26 @@ hipError_t launch_grow_copy(DevSeq oldv, DevSeq newv, int L, int nkv, int d, int
 }
 template hipError_t launch_grow_copy<f16_t>(DevSeq, DevSeq, int, int, int, int, hipStream_t);
 template hipError_t launch_grow_copy<float>(DevSeq, DevSeq, int, int, int, int, hipStream_t);
+
+template <typename T>
+__global__ void tap_kernel(const float* x, int M, int H, int tap, int n_taps, T* out) {
+  const size_t n = (size_t)M * H;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = t / H, h = t % H;
+    out[(m * n_taps + tap) * H + h] = Elem<T>::from_f(x[t]);
+  }
+}
+
+template <typename T>
+hipError_t launch_tap(const float* x, int M, int H, int tap, int n_taps, void* out, hipStream_t s) {
+  const size_t n = (size_t)M * H;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+  hipLaunchKernelGGL((tap_kernel<T>), dim3(blocks), dim3(256), 0, s, x, M, H, tap, n_taps, (T*)out);
+  return hipGetLastError();
+}
+template hipError_t launch_tap<bf16_t>(const float*, int, int, int, int, void*, hipStream_t);
+template hipError_t launch_tap<float>(const float*, int, int, int, int, void*, hipStream_t);
 
 __global__ void fill_u32_kernel(unsigned* p, size_t n, unsigned v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)

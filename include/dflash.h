@@ -132,6 +132,23 @@ dflash_status dflash_model_create(const dflash_config *cfg, const dflash_weights
                                   dflash_model **out);
 dflash_status dflash_model_destroy(dflash_model *m);
 
+/* Target model for block verification (Google Developers Blog, "Overcoming
+ * the autoregressive bottleneck" and "K-Flat"; kongchang.com "D-Flash",
+ * "System architecture"): a decoder of the same layer form as the drafter
+ * (RMSNorm, GQA attention with rotate-half RoPE, SwiGLU MLP, final RMSNorm,
+ * LM head) but causal, with no context projection.  cfg->n_feat is the
+ * number of tapped layers (0 allowed) and taps (host [n_feat], increasing
+ * layer indices) the layers whose output residual rows dflash_verify_block
+ * returns as the drafter's features, concatenated in tap order.  w->fc is
+ * ignored (may be NULL).  Packing, ownership and errors as in
+ * dflash_model_create.  Contexts of a target come from dflash_ctx_create;
+ * they hold the target's K/V cache of committed positions and accept only
+ * dflash_verify_block and dflash_commit (the drafter calls return
+ * DFLASH_E_STATE on them, and the verification calls on a drafter's). */
+dflash_status dflash_target_create(const dflash_config *cfg, const dflash_weights *w,
+                                   const int32_t *taps, const dflash_allocator *alloc, void *stream,
+                                   dflash_model **out);
+
 /* Weight bytes the hot path streams per draft block (packed matrices plus
  * gains), for roofline accounting. */
 dflash_status dflash_model_bytes(const dflash_model *m, int64_t *layer_bytes,
@@ -235,6 +252,30 @@ dflash_status dflash_accept(const int32_t *draft_ids, const int32_t *target_ids,
 dflash_status dflash_decay_ce(const void *logits, dflash_dtype dtype, const int32_t *targets,
                               int32_t rows, int32_t vocab, int32_t block, double gamma, float *loss,
                               float *ce, void *grad, void *workspace, void *stream);
+
+/* Target-side verification of a block of K1 rows per sequence: the anchor
+ * (at position ctx_len) and the K1 - 1 drafts after it (Google Developers
+ * Blog, "Overcoming the autoregressive bottleneck": one parallel forward of
+ * the target checks the whole block).  Row i attends to the committed
+ * positions and to block rows 0..i; its K/V are written to the cache at
+ * slot ctx_len + i (growing the capacity to the next power of two of
+ * ctx_len + K1 first if needed) but not committed.
+ *   block_ids  dev [batch, K1] int32 (ids outside [0, V) are clamped)
+ *   target_ids dev [batch, K1] int32 out: argmax of row i (lowest index on
+ *              ties), the target's token for position ctx_len + 1 + i
+ *   logits     dev [batch, K1, V] float32 out, or NULL
+ *   taps       dev [batch, K1, n_feat * hidden] model dtype out, or NULL:
+ *              the residual rows after each tapped layer, in tap order
+ * 1 <= K1 <= DFLASH_MAX_K.  Asynchronous on `stream`.
+ * dflash_commit then keeps the first n_acc[b] rows of sequence b's last
+ * verified block (n_acc host [batch], 0 <= n_acc[b] <= K1; normally the
+ * acceptance length tau of dflash_accept): ctx_len advances by n_acc[b]
+ * (Google Developers Blog, "Bridging the metadata gap": only accepted
+ * positions count).  A commit consumes the verification; committing again,
+ * or more rows than were verified, returns DFLASH_E_STATE. */
+dflash_status dflash_verify_block(dflash_ctx *c, const int32_t *block_ids, int32_t K1,
+                                  int32_t *target_ids, float *logits, void *taps, void *stream);
+dflash_status dflash_commit(dflash_ctx *c, const int32_t *n_acc, void *stream);
 
 /* Host copies of the state: ctx_len and cap, host [batch] each (either may
  * be NULL). */
