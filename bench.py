@@ -20,6 +20,7 @@ bounded sample of the same workload.
     python bench.py [--steps 50] [--warmup 10] [--workload 1]
     python bench.py --ksweep          # block-size sweep, one line per K
     python bench.py --decay-ce        # drafter-training loss kernel instead
+    python bench.py --verify-sweep    # target-side verification latency vs block size
 """
 from __future__ import annotations
 
@@ -63,6 +64,8 @@ def parse():
                     help="benchmark the loss-decay weighted cross-entropy (drafter training) instead")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the decay-CE oracle sample timed on the host")
+    ap.add_argument("--verify-sweep", action="store_true",
+                    help="benchmark target-side verification latency vs block size instead")
     return ap.parse_args()
 
 
@@ -315,6 +318,125 @@ def bench_decay_ce(args, torch, dfl):
     print(json.dumps(out))
 
 
+VERIFY_K1 = (16, 32, 64, 128, 256, 512, 1024)
+VERIFY_CTX, VERIFY_SEED = 4096, 1005
+
+
+def verify_cpu_baseline(shape, taps, n_layers=4, ctx=256, K1=16):
+    """The fp64 target oracle on a bounded sample: a K1-row block verified
+    against a ctx-position cache of the first n_layers layers (prefill
+    untimed), scaled to the whole target by its layer count."""
+    import synth
+    from oracle import dflash as O
+    from oracle import target as OT
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    sub = shape.replace(n_layers=n_layers)
+    w = synth.weights(sub, VERIFY_SEED)
+    m = O.Model(sub, w)
+    rng = np.random.default_rng(0)
+    st = OT.new_target_state(m)
+    OT.commit(st, OT.verify(m, st, rng.integers(0, sub.vocab, ctx)), ctx)
+    OT.verify(m, st, rng.integers(0, sub.vocab, K1))        # upcasts the weights once (untimed)
+    t0 = time.time()
+    OT.verify(m, st, rng.integers(0, sub.vocab, K1), tuple(t for t in taps if t < n_layers))
+    dt = time.time() - t0
+    scaled = dt * shape.n_layers / n_layers
+    return {"value": round(scaled * 1e3, 1), "unit": "ms per verify (scaled)", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one {K1}-row block verified in fp64 by the first {n_layers} of {shape.n_layers} layers "
+                      f"(plus LM head) over a {ctx}-position cache: {dt:.2f} s, scaled by "
+                      f"{shape.n_layers}/{n_layers}"}
+
+
+def bench_verify(args, torch, dfl):
+    """Latency of one target verification vs block size at a fixed context:
+    the pages' K-Flat claim, on a 36-layer Qwen3-4B-shaped target."""
+    import synth
+    shape = synth.QWEN3_4B_TARGET
+    taps = synth.QWEN3_4B_TAPS
+    shape = shape.replace(n_feat=len(taps))
+    t0 = time.time()
+    w = synth.weights(shape, VERIFY_SEED)
+    log(f"[bench] target weights generated in {time.time() - t0:.1f}s")
+    wd = dfl.weights_to_device(w)
+    del w
+    model = dfl.Model(shape, wd, taps=taps)
+    for k in list(wd):
+        if k != "embed":
+            del wd[k]
+    torch.cuda.empty_cache()
+    ctx = dfl.Context(model, 1)
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(VERIFY_SEED)
+    maxk = max(VERIFY_K1)
+    tgt = torch.empty(1, maxk, dtype=torch.int32, device="cuda")
+    done = 0
+    while done < VERIFY_CTX:          # prefill: verify + commit in blocks of up to 1024
+        n = min(1024, VERIFY_CTX - done)
+        ids = torch.randint(0, shape.vocab, (1, n), dtype=torch.int32, device="cuda", generator=g)
+        dfl.dflash_verify_block(ctx, ids, n, tgt[:, :n].contiguous() if n != maxk else tgt)
+        dfl.dflash_commit(ctx, [n])
+        done += n
+    torch.cuda.synchronize()
+    mb = model.bytes()
+    weight_bytes = mb["layers"] + mb["lm_head"]
+    kv_per_pos = shape.n_layers * 2 * shape.n_kv_heads * shape.head_dim * 2
+    sweep = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for K1 in VERIFY_K1:
+        ids = torch.randint(0, shape.vocab, (1, K1), dtype=torch.int32, device="cuda", generator=g)
+        out = torch.empty(1, K1, dtype=torch.int32, device="cuda")
+        for _ in range(args.warmup):
+            dfl.dflash_verify_block(ctx, ids, K1, out)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            dfl.dflash_verify_block(ctx, ids, K1, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        byt = weight_bytes + (VERIFY_CTX + K1) * kv_per_pos
+        flops = 2.0 * K1 * (weight_bytes / 2) + 4.0 * shape.n_layers * shape.n_q_heads * shape.head_dim * \
+            K1 * (VERIFY_CTX + K1 / 2)
+        sweep.append({"K1": K1, "verify_ms": round(ms, 4), "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(flops / (ms * 1e-3) / 2.5e15, 4)})
+        log(f"[bench] verify K1={K1}: {ms:.3f} ms")
+    ctx.profile(True)
+    ids = torch.randint(0, shape.vocab, (1, 16), dtype=torch.int32, device="cuda", generator=g)
+    out = torch.empty(1, 16, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        dfl.dflash_verify_block(ctx, ids, 16, out)
+    ph = {k: round(v[0] / 3, 4) for k, v in ctx.profile_read().items()}
+    ctx.profile(False)
+    lat = {r["K1"]: r["verify_ms"] for r in sweep}
+    r16 = sweep[0]
+    out = {
+        "metric": "target verification latency vs block size (36-layer Qwen3-4B-shaped target, ctx 4096)",
+        "value": r16["verify_ms"], "unit": "ms per verify at K1 = 16", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"target verify, 36 layers, H 2560, 32q/8kv x 128, I 9728, V 151936, "
+                               f"taps {list(taps)}, ctx {VERIFY_CTX}", "batch": 1, "parallelism": "1 GPU"},
+        "sweep": sweep,
+        "latency_ratio_K1_128_over_16": round(lat[128] / lat[16], 4),
+        "latency_ratio_K1_1024_over_16": round(lat[1024] / lat[16], 4),
+        "phase_ms_at_K1_16": ph,
+        "roofline": {"kernel": "whole verification at K1 = 16 (36 layers + LM head, events on the stream)",
+                     "bound": "hbm", "achieved": round((weight_bytes + (VERIFY_CTX + 16) * kv_per_pos) /
+                                                       (r16["verify_ms"] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r16["hbm_frac"], "traffic": None,
+                     "bytes_per_launch": int(weight_bytes + (VERIFY_CTX + 16) * kv_per_pos)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = verify_cpu_baseline(shape, taps)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -330,6 +452,9 @@ def main():
         if args.copy_calibration:
             copy_calibration(torch)
         bench_decay_ce(args, torch, dfl)
+        return
+    if args.verify_sweep:
+        bench_verify(args, torch, dfl)
         return
     if args.copy_calibration:
         copy_calibration(torch)

@@ -107,6 +107,13 @@ LLAMA31_8B = Shape(hidden=4096, n_layers=5, n_q_heads=32, n_kv_heads=8,
                    rope_theta=5e5, dtype="bf16", tied=False)
 
 
+# Verification target of the Qwen3-4B shape (36 layers; the drafter's
+# shape has 5), with five tapped layers spread from shallow to deep as the
+# drafter's n_feat = 5 feature sources.
+QWEN3_4B_TARGET = QWEN3_4B.replace(n_layers=36)
+QWEN3_4B_TAPS = (1, 9, 17, 25, 33)
+
+
 def _config4_ctx(seed: int, batch: int) -> Tuple[int, ...]:
     g = stream(seed, "ctx0")
     u = g.uniform(math.log(1024.0), math.log(32768.0), size=batch)
