@@ -15,6 +15,7 @@ Entry points keep the C names:
   dflash_decay_ce                  loss-decay weighted cross-entropy (training)
   dflash_target_create / Model(target=True), dflash_verify_block,
   dflash_commit                    target-side block verification
+  dflash_adapt_* / AdaptPolicy     adaptive block size (host)
 """
 from __future__ import annotations
 
@@ -70,7 +71,8 @@ EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_
            "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
            "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_step",
            "dflash_accept", "dflash_decay_ce", "dflash_target_create", "dflash_verify_block",
-           "dflash_commit",
+           "dflash_commit", "dflash_adapt_create", "dflash_adapt_destroy", "dflash_adapt_observe",
+           "dflash_adapt_choose",
            "dflash_ctx_query", "dflash_ctx_buffers", "dflash_ctx_set_persistent",
            "dflash_ctx_persistent_path", "dflash_ctx_check", "dflash_persist_trace",
            "dflash_profile_enable",
@@ -106,6 +108,13 @@ def _load() -> ctypes.CDLL:
                                   ctypes.POINTER(_Allocator), vp, ctypes.POINTER(vp)], ctypes.c_int),
         "dflash_verify_block": ([vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
         "dflash_commit": ([vp, i32p, vp], ctypes.c_int),
+        "dflash_adapt_create": ([i32, ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                 ctypes.POINTER(vp)], ctypes.c_int),
+        "dflash_adapt_destroy": ([vp], ctypes.c_int),
+        "dflash_adapt_observe": ([vp, i32, i32], ctypes.c_int),
+        "dflash_adapt_choose": ([vp, i32p, ctypes.POINTER(ctypes.c_double), i32, i32p,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "dflash_ctx_query": ([vp, i32p, i32p], ctypes.c_int),
         "dflash_ctx_buffers": ([vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                 ctypes.POINTER(vp), i32p], ctypes.c_int),
@@ -467,6 +476,43 @@ def dflash_commit(ctx: Context, n_acc: Sequence[int], stream: Optional[torch.cud
     b's cache (host counts)."""
     nn = (ctypes.c_int32 * ctx.batch)(*[int(n) for n in n_acc])
     _check("dflash_commit", lib.dflash_commit(ctx.handle, nn, _stream(stream)))
+
+
+class AdaptPolicy:
+    """dflash_adapt_create / observe / choose / destroy: the block size per
+    step from running acceptance statistics (host computation)."""
+
+    def __init__(self, kmax: int, decay: float = 0.98, min_count: float = 4.0, a0: float = 0.8,
+                 gamma0: float = 0.95):
+        h = ctypes.c_void_p()
+        _check("dflash_adapt_create", lib.dflash_adapt_create(int(kmax), float(decay), float(min_count),
+                                                              float(a0), float(gamma0), ctypes.byref(h)))
+        self.handle = h
+
+    def observe(self, K: int, tau: int) -> None:
+        _check("dflash_adapt_observe", lib.dflash_adapt_observe(self.handle, int(K), int(tau)))
+
+    def choose(self, Ks: Sequence[int], cost: Sequence[float]):
+        """(K, a, gamma, expected tokens per unit cost) for candidates Ks
+        (increasing) with per-step costs."""
+        n = len(Ks)
+        ks = (ctypes.c_int32 * max(n, 1))(*[int(k) for k in Ks])
+        cs = (ctypes.c_double * max(n, 1))(*[float(c) for c in cost])
+        K, a, g, v = ctypes.c_int32(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        _check("dflash_adapt_choose", lib.dflash_adapt_choose(self.handle, ks, cs, n, ctypes.byref(K),
+                                                              ctypes.byref(a), ctypes.byref(g), ctypes.byref(v)))
+        return K.value, a.value, g.value, v.value
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib.dflash_adapt_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def version() -> str:

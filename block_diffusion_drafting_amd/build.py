@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = ["api.hip", "gemm.hip", "gemm_qkv.hip", "gemm_swiglu.hip", "gemm_part.hip", "gemm_argmax.hip",
            "gemm_proj.hip", "attention.hip", "misc.hip", "persist.hip",
-           "loss.hip"]
+           "loss.hip", "adapt.hip"]
 LIB = os.path.join(HERE, "libdflash.so")
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 

@@ -289,6 +289,9 @@ bool valid_stream_ptrs(const dflash_weights* w, int L, bool target = false) {
 
 }  // namespace
 
+// For the host-only sources of the library (C++ linkage, not exported).
+dflash_status dflash_set_error(dflash_status st, const char* msg) { return fail(st, "%s", msg); }
+
 extern "C" {
 
 const char* dflash_version(void) { return "dflash-mi355x 0.1 (gfx950)"; }

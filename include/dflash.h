@@ -277,6 +277,39 @@ dflash_status dflash_verify_block(dflash_ctx *c, const int32_t *block_ids, int32
                                   int32_t *target_ids, float *logits, void *taps, void *stream);
 dflash_status dflash_commit(dflash_ctx *c, const int32_t *n_acc, void *stream);
 
+/* Adaptive block size (host computation; kongchang.com "D-Flash",
+ * "Ablations": a drafter trained on a large block serves smaller blocks, so
+ * the block size can follow the load; Google Developers Blog, "Scaling
+ * theory" and "Predictability": acceptance at block position i has
+ * probability a * gamma^i, the decay depending on the task).
+ *   dflash_adapt_create   kmax: largest block size observed (1..DFLASH_MAX_K);
+ *                         decay in (0, 1]: forgetting factor applied to the
+ *                         statistics at every observed step; min_count: the
+ *                         weight a position needs to enter the fit; (a0,
+ *                         gamma0) in (0, 1]: the estimate until two
+ *                         positions qualify.
+ *   dflash_adapt_observe  one step drafted at block size K (<= kmax) with
+ *                         acceptance length tau in [1, K + 1].
+ *   dflash_adapt_choose   the current (a, gamma) (weighted least squares of
+ *                         log((agreed + 1/2) / (reached + 1)) on the
+ *                         position, weights = reached, clamped to [1e-6, 1])
+ *                         and, among the n candidates Ks (host, strictly
+ *                         increasing) with per-step costs cost (host, > 0,
+ *                         e.g. draft + verify latency at that K), the K
+ *                         maximising E[tau | K] / cost(K) with
+ *                         E[tau | K] = 1 + sum_{m<=K} prod_{i<m} a gamma^i,
+ *                         the smaller K on ties; *tokens_per_cost is that
+ *                         maximum.  Outputs may be NULL.
+ * The policy is plain host memory: no device, no stream; one thread at a
+ * time per policy. */
+typedef struct dflash_adapt dflash_adapt;
+dflash_status dflash_adapt_create(int32_t kmax, double decay, double min_count, double a0, double gamma0,
+                                  dflash_adapt **out);
+dflash_status dflash_adapt_destroy(dflash_adapt *p);
+dflash_status dflash_adapt_observe(dflash_adapt *p, int32_t K, int32_t tau);
+dflash_status dflash_adapt_choose(const dflash_adapt *p, const int32_t *Ks, const double *cost, int32_t n,
+                                  int32_t *K, double *a, double *gamma, double *tokens_per_cost);
+
 /* Host copies of the state: ctx_len and cap, host [batch] each (either may
  * be NULL). */
 dflash_status dflash_ctx_query(const dflash_ctx *c, int32_t *ctx_len, int32_t *cap);
