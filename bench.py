@@ -21,6 +21,7 @@ bounded sample of the same workload.
     python bench.py --ksweep          # block-size sweep, one line per K
     python bench.py --decay-ce        # drafter-training loss kernel instead
     python bench.py --verify-sweep    # target-side verification latency vs block size
+    python bench.py --adaptive        # draft-verify loop, adaptive vs fixed block size
 """
 from __future__ import annotations
 
@@ -66,6 +67,9 @@ def parse():
                     help="rows of the decay-CE oracle sample timed on the host")
     ap.add_argument("--verify-sweep", action="store_true",
                     help="benchmark target-side verification latency vs block size instead")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="benchmark the draft-verify loop with the adaptive block size instead")
+    ap.add_argument("--loop-steps", type=int, default=300, help="steps per session of --adaptive")
     return ap.parse_args()
 
 
@@ -437,6 +441,173 @@ def bench_verify(args, torch, dfl):
     print(json.dumps(out))
 
 
+ADAPT_KS = (4, 8, 16, 32, 64)
+# acceptance regimes of one session (a, gamma, steps as a share of the
+# session): code-like, chat-like, mixed
+ADAPT_PHASES = ((0.95, 0.98, 1 / 3), (0.6, 0.85, 1 / 3), (0.9, 0.95, 1 / 3))
+
+
+def bench_adaptive(args, torch, dfl):
+    """The whole speculative loop on one GPU, per step: draft K rows
+    (drafter), verify the K + 1 rows [anchor, drafts] (36-layer target),
+    acceptance length from the seeded agreement model (a, gamma per phase),
+    commit tau rows in the target, project tau feature rows into the
+    drafter.  Block size per step from dflash_adapt_choose (costs = the
+    draft + verify latencies measured here), or fixed."""
+    import synth
+    wl = synth.workload(1)
+    dshape = wl.shape
+    tshape = synth.QWEN3_4B_TARGET.replace(n_feat=len(synth.QWEN3_4B_TAPS))
+    w = synth.weights(dshape, wl.seed)
+    dwd = dfl.weights_to_device(w)
+    dmodel = dfl.Model(dshape, dwd)
+    tw = synth.weights(tshape, VERIFY_SEED)
+    twd = dfl.weights_to_device(tw)
+    del tw
+    tmodel = dfl.Model(tshape, twd, taps=synth.QWEN3_4B_TAPS)
+    for k in list(twd):
+        if k != "embed":
+            del twd[k]
+    torch.cuda.empty_cache()
+    ctx0 = wl.ctx0[0]
+    pre_feats = torch.from_numpy(synth.prefill_features(dshape, wl.seed, 0, ctx0)).cuda()
+    kmax = max(ADAPT_KS)
+    step_feats = torch.from_numpy(synth.step_features(dshape, wl.seed, 0, 0, kmax + 1)).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(VERIFY_SEED)
+    pre_ids = torch.randint(0, tshape.vocab, (1, ctx0), dtype=torch.int32, device="cuda", generator=g)
+
+    def fresh():
+        dctx = dfl.Context(dmodel, 1)
+        dfl.dflash_project_ctx(dctx, pre_feats, [ctx0])
+        tctx = dfl.Context(tmodel, 1)
+        done = 0
+        while done < ctx0:
+            n = min(1024, ctx0 - done)
+            out = torch.empty(1, n, dtype=torch.int32, device="cuda")
+            dfl.dflash_verify_block(tctx, pre_ids[:, done:done + n].contiguous(), n, out)
+            dfl.dflash_commit(tctx, [n])
+            done += n
+        return dctx, tctx
+
+    draft = torch.empty(1, kmax, dtype=torch.int32, device="cuda")
+    vids = torch.empty(1, kmax + 1, dtype=torch.int32, device="cuda")
+    vout = torch.empty(1, kmax + 1, dtype=torch.int32, device="cuda")
+
+    def one_step(dctx, tctx, d_ids, K, anchor, tau):
+        """Enqueue one step (no host synchronisation)."""
+        dk = draft[:, :K]
+        dfl.dflash_draft_block(dctx, d_ids, K, dk)
+        vids[:, 0] = anchor
+        vids[:, 1:K + 1] = dk
+        dfl.dflash_verify_block(tctx, vids[:, :K + 1], K + 1, vout[:, :K + 1])
+        dfl.dflash_commit(tctx, [tau])
+        dfl.dflash_project_ctx(dctx, step_feats[:tau], [tau])
+
+    # per-step cost of each candidate at the starting context (ms)
+    dctx, tctx = fresh()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    costs = []
+    for K in ADAPT_KS:
+        d_ids = torch.from_numpy(synth.block_ids(wl.seed, 0, 0, K, dshape.vocab).reshape(1, K)).cuda()
+        vid = torch.randint(0, tshape.vocab, (1, K + 1), dtype=torch.int32, device="cuda", generator=g)
+        for _ in range(3):
+            dfl.dflash_draft_block(dctx, d_ids, K, draft[:, :K])
+            dfl.dflash_verify_block(tctx, vid, K + 1, vout[:, :K + 1])
+        e0.record()
+        for _ in range(10):
+            dfl.dflash_draft_block(dctx, d_ids, K, draft[:, :K])
+            dfl.dflash_verify_block(tctx, vid, K + 1, vout[:, :K + 1])
+        e1.record()
+        torch.cuda.synchronize()
+        costs.append(e0.elapsed_time(e1) / 10)
+    del dctx, tctx
+    log(f"[bench] per-step cost (draft + verify ms) at K {list(ADAPT_KS)}: {[round(c, 3) for c in costs]}")
+
+    S = args.loop_steps
+    bounds = []
+    acc = 0
+    for a, gm, share in ADAPT_PHASES:
+        n = int(round(S * share))
+        bounds.append((acc, acc + n, (a, gm)))
+        acc += n
+
+    def phase_of(t):
+        for lo, hi, ph in bounds:
+            if lo <= t < hi:
+                return ph
+        return bounds[-1][2]
+
+    def plan(policy_K):
+        """Block size, block ids and acceptance length of every step.  The
+        acceptance lengths come from the seeded agreement model, not from
+        the GPU's tokens, so the policy's choices can be made here, exactly
+        as they would be online."""
+        pol = dfl.AdaptPolicy(kmax, decay=0.95) if policy_K is None else None
+        anchor = synth.first_anchor(wl.seed, 0, dshape.vocab)
+        steps = []
+        for t in range(acc):
+            K = pol.choose(ADAPT_KS, costs)[0] if pol is not None else policy_K
+            ids = synth.block_ids(wl.seed, 0, t, K, dshape.vocab)
+            ids[0] = anchor
+            a, gm = phase_of(t)
+            dr = synth.verifier_draws(wl.seed, 0, t, K, dshape.vocab, a, gm)
+            tau = 1 + int(np.argmin(np.append(dr.agree, False)))
+            if pol is not None:
+                pol.observe(K, tau)
+            steps.append((K, ids, tau, anchor))
+            anchor = dr.bonus
+        return steps
+
+    def session(policy_K):
+        steps = plan(policy_K)
+        flat = torch.from_numpy(np.concatenate([st[1] for st in steps]).astype(np.int32)).cuda()
+        offs = np.cumsum([0] + [st[0] for st in steps])
+        dctx, tctx = fresh()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for (K, _, tau, anchor), off in zip(steps, offs):
+            one_step(dctx, tctx, flat[off:off + K].view(1, K), K, anchor, tau)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        tokens = sum(st[2] for st in steps)
+        return tokens / wall, wall * 1e3 / acc, tokens / acc, [st[0] for st in steps]
+
+    results = {}
+    for K in ADAPT_KS:
+        results[K] = session(K)
+        log(f"[bench] fixed K={K}: {results[K][0]:.1f} accepted tok/s, {results[K][1]:.3f} ms/step, "
+            f"mean tau {results[K][2]:.2f}")
+    ad = session(None)
+    log(f"[bench] adaptive: {ad[0]:.1f} accepted tok/s, {ad[1]:.3f} ms/step, mean tau {ad[2]:.2f}")
+    per_phase = []
+    for lo, hi, ph in bounds:
+        ks = ad[3][lo:hi]
+        per_phase.append({"a": ph[0], "gamma": ph[1], "steps": hi - lo,
+                          "K_counts": {str(k): ks.count(k) for k in ADAPT_KS if ks.count(k)}})
+    best_fixed = max(ADAPT_KS, key=lambda k: results[k][0])
+    out = {
+        "metric": "accepted tokens/s of the draft-verify loop with the adaptive block size "
+                  "(Qwen3-4B-shaped drafter + 36-layer target, one GPU)",
+        "value": round(ad[0], 1), "unit": "accepted tok/s", "n_gpus": 1, "steps": acc, "warmup": 0,
+        "ms_per_step": round(ad[1], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"draft-verify loop, ctx {ctx0}, candidates K {list(ADAPT_KS)}, acceptance "
+                               f"a*gamma^i in phases {[(p[0], p[1]) for p in ADAPT_PHASES]}, policy decay 0.95",
+                   "batch": 1, "parallelism": "1 GPU"},
+        "cost_ms_per_step": {str(k): round(c, 4) for k, c in zip(ADAPT_KS, costs)},
+        "fixed_K": {str(k): {"tok_s": round(results[k][0], 1), "ms_per_step": round(results[k][1], 4),
+                             "mean_tau": round(results[k][2], 3)} for k in ADAPT_KS},
+        "adaptive_mean_tau": round(ad[2], 3),
+        "adaptive_over_K16": round(ad[0] / results[16][0], 4),
+        "adaptive_over_best_fixed": round(ad[0] / results[best_fixed][0], 4),
+        "best_fixed_K": best_fixed,
+        "adaptive_K_per_phase": per_phase,
+    }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -455,6 +626,9 @@ def main():
         return
     if args.verify_sweep:
         bench_verify(args, torch, dfl)
+        return
+    if args.adaptive:
+        bench_adaptive(args, torch, dfl)
         return
     if args.copy_calibration:
         copy_calibration(torch)
