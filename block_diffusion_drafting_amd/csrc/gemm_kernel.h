@@ -252,11 +252,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
   // wave-uniform values held in scalar registers, so that the batch loop's
   // branches are scalar and the loads are never under an exec mask
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int u = blockIdx.x;
-  const int s = u % g.nsplit;
-  u /= g.nsplit;
-  const int ng = u % g.n_groups;
-  const int mg = u / g.n_groups;
+  // Work unit (tile group ng, split s) and m-group mg of this workgroup.
+  // With several m-groups, the m-groups of one unit share blockIdx % 8 (one
+  // XCD, as workgroups are dealt to the eight XCDs round robin) and sit
+  // within 8 * m_groups consecutive blocks, so they run together and all
+  // but one read the unit's weights from that XCD's L2: the weights stream
+  // from HBM about once rather than once per m-group.  Blocks past the
+  // last unit (the grid is padded to a multiple of 8 units) do nothing.
+  int s, ng, mg;
+  if (g.m_groups > 1) {
+    const int q = (int)(blockIdx.x >> 3);
+    const int unit = (q / g.m_groups) * 8 + (int)(blockIdx.x & 7);
+    if (unit >= g.n_groups * g.nsplit) return;
+    mg = q % g.m_groups;
+    s = unit % g.nsplit;
+    ng = unit / g.nsplit;
+  } else {
+    int u = blockIdx.x;
+    s = u % g.nsplit;
+    u /= g.nsplit;
+    ng = u % g.n_groups;
+    mg = u / g.n_groups;
+  }
   // balanced tile ranges: group ng owns tiles [tile0, tile0 + nt), nt <= NTG
   const int tile0 = (int)((long)ng * g.W.n_tiles / g.n_groups);
   const int nt = __builtin_amdgcn_readfirstlane((int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0);
@@ -445,7 +462,9 @@ struct HotChk {
 template <typename T, int MTT, int NTG, int EPI, bool ROW, bool SPLIT, int WAVES, int CHK,
           bool PIPE = false>
 inline hipError_t launch_v(const GemmPlan& p, const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
-  dim3 grid((unsigned)p.n_groups * p.m_groups * p.nsplit);
+  // several m-groups: units padded to a multiple of 8 (see the kernel)
+  const unsigned units = (unsigned)p.n_groups * p.nsplit;
+  dim3 grid(p.m_groups > 1 ? (units + 7u) / 8u * 8u * (unsigned)p.m_groups : units);
   hipLaunchKernelGGL((gemm_kernel<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>), grid, dim3(WAVES * 64), 0,
                      s, g, e);
   return hipGetLastError();
