@@ -140,8 +140,10 @@ struct dflash_ctx {
   // L2 warm-up by the spare blocks of latency-bound kernels (fragments per
   // product wave): output projection, next QKV, LM head
   int warm_o = 16, warm_qkv = 12, warm_lm = 2;
-  // attention grid: 8-wave workgroup equivalents per compute unit
+  // attention grid: 8-wave workgroup equivalents per compute unit, and the
+  // shortest key split (a multiple of 64)
   int attn_wgs_per_cu = 2;
+  int attn_min_split = 128;
   // persistent single-launch draft block (see persist.hip)
   struct Persist {
     bool enabled = false;   // opt in: measured slower than the per-product kernels
@@ -462,6 +464,9 @@ static dflash_status alloc_seq(dflash_ctx* c, int b, int cap, DevSeq& out) {
   const dflash_model* m = c->m;
   const int phys = cap < 64 ? 64 : cap;
   const size_t ces = m->ces;
+  // attention addresses one layer and KV head's slab with 32-bit offsets
+  if ((size_t)phys * m->cfg.head_dim * ces >= ((size_t)1 << 31))
+    return fail(DFLASH_E_ARG, "context capacity %d exceeds the per-head cache slab limit (2^31 bytes)", cap);
   const size_t kvn = (size_t)m->cfg.n_layers * m->cfg.n_kv_heads * phys * m->cfg.head_dim;
   DevSeq v{};
   v.ctx_len = c->seq[b].ctx_len;
@@ -507,6 +512,7 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
   c->warm_qkv = env_int("DFLASH_WARM_QKV", c->warm_qkv, 0, 64);
   c->warm_lm = env_int("DFLASH_WARM_LM", c->warm_lm, 0, 64);
   c->attn_wgs_per_cu = env_int("DFLASH_ATTN_WGS_PER_CU", c->attn_wgs_per_cu, 1, 16);
+  c->attn_min_split = round_up(env_int("DFLASH_ATTN_MIN_SPLIT", c->attn_min_split, 128, 1 << 20), 64);
   c->seq_dev = (DevSeq*)c->alloc.get(sizeof(DevSeq) * batch);
   if (!c->seq_dev) {
     delete c;
@@ -788,7 +794,7 @@ static dflash_status persist_draft(dflash_ctx* c, const int32_t* ids, int K, int
   // whose (sequence, KV head, split) units fit one round of the grid
   int max_len = 0;
   for (int b = 0; b < B; ++b) max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
-  int chunk = 128;
+  int chunk = c->attn_min_split;
   for (;; chunk += 64) {
     int64_t units = 0;
     for (int b = 0; b < B; ++b) units += (int64_t)nkv * ((c->seq[b].ctx_len + chunk - 1) / chunk + (K + chunk - 1) / chunk);
@@ -955,8 +961,8 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   const int qgroups = (qtiles + 3) / 4;
   int max_len = 0;
   for (int b = 0; b < B; ++b) max_len = c->seq[b].ctx_len > max_len ? c->seq[b].ctx_len : max_len;
-  // Keys per split: the smallest multiple of 64, at least 128, whose
-  // workgroups fit one round of the chip (two 4-wave workgroups or one
+  // Keys per split: the smallest multiple of 64, at least the minimum (128),
+  // whose workgroups fit one round of the chip (two 4-wave workgroups or one
   // 8-wave workgroup per CU); at short contexts the split count, not the
   // split length, sets the cost of the combine.
   const int qg_per_wg = qgroups > 1 ? 2 : 1;
@@ -965,7 +971,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   auto splits = [&](int len, int ch) {
     return vo.on ? (len + K + ch - 1) / ch : (len + ch - 1) / ch + (K + ch - 1) / ch;
   };
-  int chunk = 128;
+  int chunk = c->attn_min_split;
   for (;; chunk += 64) {
     int64_t wgs = 0;
     for (int b = 0; b < B; ++b) wgs += wg_per_split * splits(c->seq[b].ctx_len, chunk);

@@ -137,38 +137,52 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
   // Chunk staging through registers, two chunks in flight: while chunk c
   // is computed from LDS, the loads of chunks c+1 and c+2 are outstanding
   // in two register sets; chunk c+1 is stored to the other LDS buffer once
-  // c is done.  Keys at or past the split end load as zero (K rows and V^T
-  // columns).
+  // c is done.  Every lane issues the same loads on every path, so the wait
+  // before a store covers only the older set: a chunk starts at a multiple
+  // of 64 keys below the row length, and both the cache rows (a power of two
+  // >= 64) and the block rows (padded to 64) are multiples of 64, so the
+  // whole chunk is in bounds.  Keys at or past the split end are zeroed
+  // when the chunk is stored to LDS (K rows and V^T columns).  Offsets are
+  // 32-bit from the (uniform) slab base: a slab of one layer and KV head
+  // holds under 2^31 bytes (checked where the caches are allocated).
   struct Regs {
     u32x4 kr[KPT], vr[VPT];
   };
-  auto gload = [&](Regs& rg, int c0, int cend) {
+  auto gload = [&](Regs& rg, int c0) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int t = threadIdx.x + j * NTH;
       const int row = t / KP_ROW, pc = t % KP_ROW;
-      rg.kr[j] = (c0 + row < cend) ? gld16((const uint8_t*)(kbase + (size_t)(c0 + row) * D) + pc * 16)
-                                   : u32x4{0u, 0u, 0u, 0u};
+      rg.kr[j] = gld16((const uint8_t*)kbase + ((uint32_t)(c0 + row) * (D * ES) + pc * 16));
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int t = threadIdx.x + j * NTH;
       const int dr = t / VP_ROW, pc = t % VP_ROW;
-      const int key = c0 + pc * EPP;
-      const T* src = vbase + (size_t)dr * vstride + key;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (key + EPP <= cend) {
-        v = gld16(src);
-      } else if (key < cend) {
-        T tmp[EPP];
-#pragma unroll
-        for (int e2 = 0; e2 < EPP; ++e2) tmp[e2] = (key + e2 < cend) ? gld(src + e2) : (T)0;
-        v = *(const u32x4*)tmp;
-      }
-      rg.vr[j] = v;
+      rg.vr[j] = gld16((const uint8_t*)vbase + ((uint32_t)(dr * vstride + c0 + pc * EPP) * ES));
     }
   };
-  auto lstore = [&](const Regs& rg, int buf) {
+  auto lstore = [&](Regs& rg, int buf, int c0, int cend) {
+    if (cend - c0 < CHUNK_KEYS) {   // last chunk of the split (uniform)
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int t = threadIdx.x + j * NTH;
+        if (c0 + t / KP_ROW >= cend) rg.kr[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int t = threadIdx.x + j * NTH;
+        const int key = c0 + (t % VP_ROW) * EPP;
+        if (key + EPP > cend) {
+          T tmp[EPP];
+          __builtin_memcpy(tmp, &rg.vr[j], 16);
+#pragma unroll
+          for (int e2 = 0; e2 < EPP; ++e2)
+            if (key + e2 >= cend) tmp[e2] = (T)0;
+          __builtin_memcpy(&rg.vr[j], tmp, 16);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int t = threadIdx.x + j * NTH;
@@ -254,42 +268,40 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   };
-  auto chunk_range = [&](int c, int& c0, int& cend) {
-    c0 = k0 + c * CHUNK_KEYS;
-    cend = min(k1, c0 + CHUNK_KEYS);
-  };
 
-  const int nchunks = (k1 - k0 + CHUNK_KEYS - 1) / CHUNK_KEYS;
+  const int nchunks = (k1 - k0 + CHUNK_KEYS - 1) / CHUNK_KEYS;   // >= 1
+  auto cbeg = [&](int c) { return k0 + c * CHUNK_KEYS; };
+  auto cfin = [&](int c) { return min(k1, k0 + (c + 1) * CHUNK_KEYS); };
   Regs r0, r1;
-  int c0, cend;
-  chunk_range(0, c0, cend);
-  gload(r0, c0, cend);
-  if (nchunks > 1) {
-    chunk_range(1, c0, cend);
-    gload(r1, c0, cend);
-  }
-  lstore(r0, 0);
+  gload(r0, cbeg(0));
+  gload(r1, cbeg(nchunks > 1 ? 1 : 0));   // a one-chunk split loads it twice
+  lstore(r0, 0, cbeg(0), cfin(0));
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    // chunk c in LDS buffer 0, chunk c+1 in flight in r1
+  // Steady state, loads unconditional: chunk c in LDS buffer 0, chunk c+1
+  // in flight in r1, and chunks c+2 and c+3 exist.
+  int c = 0;
+  for (; c + 3 < nchunks; c += 2) {
+    gload(r0, cbeg(c + 2));
+    compute(cbeg(c), cfin(c), 0);
+    lstore(r1, 1, cbeg(c + 1), cfin(c + 1));
+    __syncthreads();
+    gload(r1, cbeg(c + 3));
+    compute(cbeg(c + 1), cfin(c + 1), 1);
+    lstore(r0, 0, cbeg(c + 2), cfin(c + 2));
+    __syncthreads();
+  }
+  // The last one to three chunks: c in buffer 0, c+1 (if any) in r1.
+  if (c + 2 < nchunks) gload(r0, cbeg(c + 2));
+  compute(cbeg(c), cfin(c), 0);
+  if (c + 1 < nchunks) {
+    lstore(r1, 1, cbeg(c + 1), cfin(c + 1));
+    __syncthreads();
+    compute(cbeg(c + 1), cfin(c + 1), 1);
     if (c + 2 < nchunks) {
-      chunk_range(c + 2, c0, cend);
-      gload(r0, c0, cend);
+      lstore(r0, 0, cbeg(c + 2), cfin(c + 2));
+      __syncthreads();
+      compute(cbeg(c + 2), cfin(c + 2), 0);
     }
-    chunk_range(c, c0, cend);
-    compute(c0, cend, 0);
-    if (c + 1 < nchunks) lstore(r1, 1);
-    __syncthreads();
-    if (c + 1 >= nchunks) break;
-    // chunk c+1 in LDS buffer 1, chunk c+2 in flight in r0
-    if (c + 3 < nchunks) {
-      chunk_range(c + 3, c0, cend);
-      gload(r1, c0, cend);
-    }
-    chunk_range(c + 1, c0, cend);
-    compute(c0, cend, 1);
-    if (c + 2 < nchunks) lstore(r0, 0);
-    __syncthreads();
   }
   l_run = wave_xor_sum16_32(l_run);
 

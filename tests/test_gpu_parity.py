@@ -92,6 +92,21 @@ def test_padding_rows_never_leak():
     assert np.all(np.isfinite(g["logits"]))
 
 
+@pytest.mark.parametrize("K", [16, 37])
+def test_small_bf16_long_splits_poisoned(monkeypatch, K):
+    """Key splits of 1024 (16 chunks of 64: the staged attention pipeline's
+    steady state and drain), ragged contexts whose last chunk is partial,
+    NaN in every cache row past ctx_len; K = 16 (one query group, key halves
+    per wave) and 37 (two query groups, one of them padding)."""
+    say(f"case: long splits K={K}")
+    monkeypatch.setenv("DFLASH_ATTN_MIN_SPLIT", "1024")
+    p = Pair(SMALL, 41, 2, gain_std=0.1)
+    _prefill(p, [1500, 2111])
+    p.poison_padding()
+    g, _ = p.compare(_ids(42, 2, K, SMALL.vocab))
+    assert np.all(np.isfinite(g["logits"]))
+
+
 def test_non_causal_through_abi():
     """Changing the last block token changes row 0's logits."""
     say("case: non-causal")

@@ -112,6 +112,23 @@ def test_verify_bf16_batch2_ragged_contexts(K1):
         p.commit([K1 if step == 0 else rng.integers(0, K1 + 1), rng.integers(0, K1 + 1)])
 
 
+@pytest.mark.parametrize("K1", [16, 40])
+def test_verify_bf16_d128_long_splits(monkeypatch, K1):
+    """head_dim 128 with bf16 weights (fp16 attention operands staged by
+    direct loads to LDS), causal, with 1024-key splits: a 700-row prefill
+    (11 chunks) and blocks over ragged contexts of several chunks each."""
+    say(f"verify bf16 d128 long splits K1={K1}")
+    monkeypatch.setenv("DFLASH_ATTN_MIN_SPLIT", "1024")
+    shape = SMALL_T.replace(head_dim=128)
+    p = VerifyPair(shape, (0, 2), 2, seed=26)
+    rng = np.random.default_rng(6)
+    p.check(_ids(rng, 2, 700, shape.vocab), "prefill")
+    p.commit([700, 431])
+    for step in range(2):
+        p.check(_ids(rng, 2, K1, shape.vocab), f"step{step}")
+        p.commit([rng.integers(0, K1 + 1), K1])
+
+
 def test_verify_cache_holds_the_committed_keys():
     """After verify + commit the cache rows [0, ctx_len) are the committed
     rows' RoPE'd keys and values (fp32 model: compared to 1e-4)."""
