@@ -965,9 +965,15 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   // whose workgroups fit one round of the chip (two 4-wave workgroups or one
   // 8-wave workgroup per CU); at short contexts the split count, not the
   // split length, sets the cost of the combine.
-  const int qg_per_wg = qgroups > 1 ? 2 : 1;
+  // Rounds (measured): one-group workgroups (4 waves, two per CU) take
+  // attn_wgs_per_cu rounds; workgroups of two or four query groups carry
+  // enough work per chunk that one round of longer splits beats two of short
+  // ones, except a non-causal block of more than 256 rows, whose own keys
+  // form splits too long to sit beside one-round context splits.
+  const int qg_per_wg = attn_groups_per_wg(ces, qgroups);
   const int64_t wg_per_split = (int64_t)nkv * ((qgroups + qg_per_wg - 1) / qg_per_wg);
-  const int64_t round_wgs = (qg_per_wg == 1 ? 2 : 1) * (int64_t)c->attn_wgs_per_cu * 256;
+  const int rounds = qg_per_wg == 1 || (!vo.on && K > 256) ? c->attn_wgs_per_cu : (c->attn_wgs_per_cu + 1) / 2;
+  const int64_t round_wgs = (qg_per_wg == 1 ? 2 : 1) * (int64_t)rounds * 256;
   auto splits = [&](int len, int ch) {
     return vo.on ? (len + K + ch - 1) / ch : (len + ch - 1) / ch + (K + ch - 1) / ch;
   };

@@ -42,8 +42,11 @@ size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d) {
 }
 
 // Two waves per SIMD (two 4-wave or one 8-wave workgroup per compute unit,
-// as the grid is planned): at most 256 registers per wave.
-template <typename T, int D, int QG>
+// as the grid is planned): at most 256 registers per wave.  QG: 4-wave
+// groups of the workgroup (1 or 2); QT: query tiles per wave (1 or 2).  A
+// workgroup serves QG * QT query groups of 64 rows, and with QT = 2 every K
+// or V^T fragment read from LDS feeds two MFMAs.
+template <typename T, int D, int QG, int QT>
 __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnArgs a) {
   using E = Elem<T>;
   constexpr int CHUNK_KEYS = chunk_keys<T, D>();
@@ -70,17 +73,20 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
                   (lds_void_t*)(kl[0] + (threadIdx.x >> 6) * 1024));
     return;
   }
-  // QG query groups share each staged chunk: wave w is query tile w % 4 of
-  // query group qgp * QG + w / 4
+  // QG * QT query groups share each staged chunk: tile j of wave w is query
+  // tile w % 4 of query group qgp * QG * QT + j * QG + w / 4
+  constexpr int GPW = QG * QT;
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;
   const int g4 = lane >> 4, col = lane & 15;
   // Workgroups of the same (sequence, KV head, split) and different query
   // groups read the same keys; blocks are dealt to the 8 XCDs round-robin,
   // so they are numbered to share blockIdx % 8 (one L2) -- see attn_grid.
-  const int nqgp = (a.qgroups + QG - 1) / QG;
+  const int nqgp = (a.qgroups + GPW - 1) / GPW;
   const int lo = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
-  const int qg = (rest % nqgp) * QG + (int)(threadIdx.x >> 8);
+  int qg[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) qg[j] = (rest % nqgp) * GPW + j * QG + (int)(threadIdx.x >> 8);
   int u = (rest / nqgp) * 8 + lo;
   if (u >= a.B * a.nkv * a.max_splits) return;
   const int s = u % a.max_splits;
@@ -111,28 +117,34 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
     k1 = min(a.K, k0 + a.chunk);
   }
 
-  // query rows of this wave: r = qtile*16 + col -> head h, block row i
+  // query rows of tile j: r = qtile*16 + col -> head h, block row i
   const int rep = a.nq / a.nkv;
   const int nrows = a.K * rep;
-  const int qt = qg * 4 + wave;
-  const int r = qt * 16 + col;
-  const bool row_ok = qg < a.qgroups && r < nrows;
-  const int h = g * rep + (row_ok ? r / a.K : 0);
-  const int i = row_ok ? r % a.K : 0;
-  // causal form: this lane's query (block row i) sees cache keys 0..ctx_len+i
-  const int key_lim = a.causal ? ctx_len + i : 0x7FFFFFFF;
-  u32x4 qf[NFD];
-  {
+  u32x4 qf[QT][NFD];
+  int key_lim[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    const int r = (qg[j] * 4 + wave) * 16 + col;
+    const bool row_ok = qg[j] < a.qgroups && r < nrows;
+    const int h = g * rep + (row_ok ? r / a.K : 0);
+    const int i = row_ok ? r % a.K : 0;
+    // causal form: this lane's query (block row i) sees cache keys 0..ctx_len+i
+    key_lim[j] = a.causal ? ctx_len + i : 0x7FFFFFFF;
     const T* qp = (const T*)a.q + ((size_t)(b * a.K + i) * a.nq + h) * D;
 #pragma unroll
     for (int f = 0; f < NFD; ++f)
-      qf[f] = row_ok ? gld16(qp + f * E::KB + g4 * E::KPL) : u32x4{0u, 0u, 0u, 0u};
+      qf[j][f] = row_ok ? gld16(qp + f * E::KB + g4 * E::KPL) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  f32x4 o[NDT];
+  f32x4 o[QT][NDT];
+  float m_run[QT], l_run[QT];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int j = 0; j < QT; ++j) {
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
 
   // Chunk staging through registers, two chunks in flight: while chunk c
   // is computed from LDS, the loads of chunks c+1 and c+2 are outstanding
@@ -194,77 +206,91 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
       *(u32x4*)(vl[buf] + (t / VP_ROW) * VROW + (t % VP_ROW) * 16) = rg.vr[j];
     }
   };
-  // online softmax and P.V over chunk [c0, cend) held in LDS buffer buf
+  // online softmax and P.V over chunk [c0, cend) held in LDS buffer buf;
+  // each K and V^T fragment read from LDS serves the wave's QT tiles
   auto compute = [&](int c0, int cend, int buf) {
     const uint8_t* klb = kl[buf];
     const uint8_t* vlb = vl[buf];
 #pragma unroll
     for (int sub = 0; sub < CHUNK_KEYS / KP; ++sub) {
       const int kb = sub * KP;  // key offset of this P.V step within the chunk
-      float sv[8];
-      int nv;
+      constexpr int NV = ES == 2 ? 8 : 4;   // keys per lane of this step
+      float sv[QT][NV];
       if constexpr (ES == 2) {
         // two S^T tiles: tile A rows -> keys 8*(row/4) + row%4, tile B -> +4
         const int rowA = kb + ((col >> 2) << 3) + (col & 3);
         const int rowB = rowA + 4;
-        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 sa[QT], sb[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) sa[j] = sb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int f = 0; f < NFD; ++f) {
           const u32x4 ka = *(const u32x4*)(klb + rowA * KROW + f * 64 + g4 * 16);
           const u32x4 kb2 = *(const u32x4*)(klb + rowB * KROW + f * 64 + g4 * 16);
-          sa = E::mma(ka, qf[f], sa);
-          sb = E::mma(kb2, qf[f], sb);
+#pragma unroll
+          for (int j = 0; j < QT; ++j) {
+            sa[j] = E::mma(ka, qf[j][f], sa[j]);
+            sb[j] = E::mma(kb2, qf[j][f], sb[j]);
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sv[j] = sa[j];
-          sv[4 + j] = sb[j];
-        }
-        nv = 8;
+        for (int j = 0; j < QT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[j][e] = sa[j][e];
+            sv[j][4 + e] = sb[j][e];
+          }
       } else {
         const int row = kb + col;
-        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 sa[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) sa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int f = 0; f < NFD; ++f) {
           const u32x4 ka = *(const u32x4*)(klb + row * KROW + f * 64 + g4 * 16);
-          sa = E::mma(ka, qf[f], sa);
+#pragma unroll
+          for (int j = 0; j < QT; ++j) sa[j] = E::mma(ka, qf[j][f], sa[j]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sv[j] = sa[j];
-        nv = 4;
-      }
-      // lane holds keys c0 + kb + g4*nv + j for query column `col`
-      float mx = -INFINITY;
+        for (int j = 0; j < QT; ++j)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < nv) {
-          const int key = c0 + kb + g4 * nv + j;
-          sv[j] = (key < cend && key <= key_lim) ? sv[j] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sv[j]);
+          for (int e = 0; e < 4; ++e) sv[j][e] = sa[j][e];
+      }
+      // lane holds keys c0 + kb + g4*NV + e for query column `col`
+      u32x4 pf[QT];
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const int key = c0 + kb + g4 * NV + e;
+          sv[j][e] = (key < cend && key <= key_lim[j]) ? sv[j][e] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[j][e]);
         }
-      }
-      mx = wave_xor_max16_32(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_safe);
-      float pv[8];
-      float psum = 0.f;
+        mx = wave_xor_max16_32(mx);
+        const float m_new = fmaxf(m_run[j], mx);
+        const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run[j] - m_safe);
+        float pv[8];
+        float psum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < nv) {
-          pv[j] = exp2f(sv[j] - m_safe);
-          psum += pv[j];
+        for (int e = 0; e < 8; ++e) {
+          if (e < NV) {
+            pv[e] = exp2f(sv[j][e] - m_safe);
+            psum += pv[e];
+          }
         }
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+        l_run[j] = l_run[j] * alpha + psum;
+        m_run[j] = m_new;
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) o[t] *= alpha;
-      const u32x4 pf = f_to_frag<T>(pv);
+        for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
+        pf[j] = f_to_frag<T>(pv);
+      }
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
         const u32x4 vf = *(const u32x4*)(vlb + (t * 16 + col) * VROW + kb * ES + g4 * 16);
-        o[t] = E::mma(vf, pf, o[t]);
+#pragma unroll
+        for (int j = 0; j < QT; ++j) o[j][t] = E::mma(vf, pf[j], o[j][t]);
       }
     }
   };
@@ -303,19 +329,299 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
       compute(cbeg(c + 2), cfin(c + 2), 0);
     }
   }
-  l_run = wave_xor_sum16_32(l_run);
-
-  // o[t][j] = O^T[d = 16t + 4*g4 + j][query column col]; every split writes
-  // its partial (m, l, O); attn_combine merges them in split order.
-  if (qg >= a.qgroups) return;   // padding query group of an odd count
-  const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
+  // o[j][t][e] = O^T[d = 16t + 4*g4 + e][query column col] of tile j; every
+  // split writes its partial (m, l, O); attn_combine merges them in split
+  // order.  Padding query groups (past the count) write nothing.
   const size_t wstride = (size_t)D * 16 + 32;
-  float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) *(f32x4*)(pp + (t * 64 + lane) * 4) = o[t];
-  if (g4 == 0) {
-    pp[D * 16 + col] = m_run;
-    pp[D * 16 + 16 + col] = l_run;
+  for (int j = 0; j < QT; ++j) {
+    const float l_sum = wave_xor_sum16_32(l_run[j]);
+    if (qg[j] >= a.qgroups) continue;
+    const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg[j];
+    float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) *(f32x4*)(pp + (t * 64 + lane) * 4) = o[j][t];
+    if (g4 == 0) {
+      pp[D * 16 + col] = m_run[j];
+      pp[D * 16 + 16 + col] = l_sum;
+    }
+  }
+}
+
+// Attention for many query rows (at least four query groups of 64 rows)
+// with fp16 operands and head_dim 128.  The work is bound by the MFMA
+// chains and the softmax between them, so each wave carries two 16-row
+// query tiles (every K or V^T fragment read from LDS feeds two MFMAs and
+// the two tiles' chains interleave) and a workgroup of 8 waves serves four
+// query groups.  Two tiles' accumulators leave no registers for data in
+// transit, so chunks (64 keys: K rows 16 KiB, V^T columns 16 KiB) are loaded
+// straight into one of MQ_STAGES LDS stages by 16-byte-per-lane direct
+// loads, MQ_STAGES - 1 chunks in flight while one is computed.  A direct
+// load writes 1 KiB of consecutive LDS per wave instruction, so rows are not
+// padded; the 16-byte pieces of a row are XOR-permuted instead (the lane's
+// global address picks the piece), so that the fragment reads of 16 rows
+// hit 16 different bank groups:
+//   K stage: row r (key), piece p (16 bytes of d) at r * 256 + 16 * (p ^ kswz(r));
+//   V stage: row t (d), piece p (8 keys) at t * 128 + 16 * (p ^ vswz(t)).
+// Tile j of wave w is query tile w % 4 of query group 4 * qgp + 2 j + w / 4;
+// the split partials have the layout of the register-staged kernel.
+constexpr int MQ_STAGES = 4;
+
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+__device__ __forceinline__ int vswz(int t) { return (t >> 1) & 7; }
+
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima = no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane direct load to LDS: lane l's 16 bytes at base + off
+// go to LDS byte address lds + 16 l.  base and lds must be wave-uniform
+// (they are read from the first lane).  Issued through inline assembly: the
+// compiler would treat a pending direct load as a pending LDS store and wait
+// for every one of them at each barrier and LDS read; it does not count
+// these, so their waits are explicit (its own waits for the loads it knows
+// only become more conservative).
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  // readfirstlane returns int: each half goes through uint32_t so that the
+  // low half is not sign-extended into the high one
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b64 >> 32));
+  const uint64_t sb = (uint64_t)lo | ((uint64_t)hi << 32);
+  const uint32_t sl = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(sb), "s"(sl)
+               : "memory", "m0");
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attention_mq_kernel(AttnArgs a) {
+  using T = f16_t;
+  using E = Elem<T>;
+  constexpr int D = 128, QT = 2, NS = MQ_STAGES;
+  constexpr int CK = 64;                 // keys per chunk
+  constexpr int KBYTES = CK * D * 2;     // 16 KiB of K rows
+  constexpr int SBYTES = 2 * KBYTES;     // one stage: K rows and V^T columns
+  constexpr int NFD = D * 2 / 64;        // 32-element d steps of S^T = K Q^T
+  constexpr int NDT = D / 16;            // 16-row d tiles of O^T
+  constexpr int LPW = KBYTES / 1024 / 8; // direct loads per wave per half-stage (2)
+  static_assert(NS >= 2 && NS * SBYTES <= 160 * 1024, "stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES];
+
+  const int w = (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a.warm.w && (int)blockIdx.x >= a.warm.first) {
+    warm_consumer(a.warm, (int)blockIdx.x - a.warm.first, 8, w, lane, (lds_void_t*)(lds + w * 1024));
+    return;
+  }
+  const int g4 = lane >> 4, col = lane & 15;
+  const int wave = w & 3;                       // query tile within its group
+  const int nqgp = (a.qgroups + 3) / 4;
+  const int lo = blockIdx.x & 7;
+  const int rest = blockIdx.x >> 3;
+  int qg[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) qg[j] = (rest % nqgp) * 4 + 2 * j + (w >> 2);
+  int u = (rest / nqgp) * 8 + lo;
+  if (u >= a.B * a.nkv * a.max_splits) return;
+  const int s = u % a.max_splits;
+  u /= a.max_splits;
+  const int g = u % a.nkv;
+  const int b = u / a.nkv;
+
+  const DevSeq sq = a.seqs[b];
+  const int ctx_len = sq.ctx_len;
+  int n_cs, n_s;
+  attn_split_counts(a, ctx_len, n_cs, n_s);
+  if (s >= n_s) return;
+
+  const T* kbase;
+  const T* vbase;
+  int vstride, k0, k1;
+  if (s < n_cs) {
+    kbase = (const T*)sq.k + ((size_t)a.layer * a.nkv + g) * sq.phys * D;
+    vbase = (const T*)sq.vt + ((size_t)a.layer * a.nkv + g) * D * sq.phys;
+    vstride = sq.phys;
+    k0 = s * a.chunk;
+    k1 = min(a.causal ? ctx_len + a.K : ctx_len, k0 + a.chunk);
+  } else {
+    kbase = (const T*)a.bk + ((size_t)b * a.nkv + g) * a.Kpad * D;
+    vbase = (const T*)a.bvt + ((size_t)b * a.nkv + g) * D * a.Kpad;
+    vstride = a.Kpad;
+    k0 = (s - n_cs) * a.chunk;
+    k1 = min(a.K, k0 + a.chunk);
+  }
+
+  const int rep = a.nq / a.nkv;
+  const int nrows = a.K * rep;
+  u32x4 qf[QT][NFD];
+  int key_lim[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    const int r = (qg[j] * 4 + wave) * 16 + col;
+    const bool row_ok = qg[j] < a.qgroups && r < nrows;
+    const int h = g * rep + (row_ok ? r / a.K : 0);
+    const int i = row_ok ? r % a.K : 0;
+    key_lim[j] = a.causal ? ctx_len + i : 0x7FFFFFFF;
+    const T* qp = (const T*)a.q + ((size_t)(b * a.K + i) * a.nq + h) * D;
+#pragma unroll
+    for (int f = 0; f < NFD; ++f)
+      qf[j][f] = row_ok ? gld16(qp + f * E::KB + g4 * E::KPL) : u32x4{0u, 0u, 0u, 0u};
+  }
+  wait_vm<0>();   // the queries, before any direct load is outstanding
+
+  // Direct loads of chunk c into stage c % NS: wave w fills K blocks 2w,
+  // 2w+1 (four key rows each) and V^T blocks 2w, 2w+1 (eight d rows each).
+  // A chunk starts at a multiple of 64 keys below the row length, which is
+  // a multiple of 64 for both the caches (a power of two >= 64) and the
+  // block buffers (padded to 64), so every load is in bounds; keys past the
+  // split end are masked when computed.  Offsets are 32-bit from the
+  // uniform slab base (a slab is under 2^31 bytes, checked where the caches
+  // are allocated).
+  const uint8_t* kb8 = (const uint8_t*)kbase;
+  const uint8_t* vb8 = (const uint8_t*)vbase;
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int blk = w * LPW + j;
+    const int kr = blk * 4 + (lane >> 4), kp = (lane & 15) ^ kswz(kr);
+    koff[j] = (uint32_t)(kr * D * 2 + kp * 16);
+    const int vr = blk * 8 + (lane >> 3), vp = (lane & 7) ^ vswz(vr);
+    voff[j] = (uint32_t)(vr * vstride * 2 + vp * 16);
+  }
+  auto issue = [&](int c) {
+    const uint32_t c0 = (uint32_t)(k0 + c * CK);
+    const uint32_t st = (uint32_t)(uintptr_t)(lds + (c % NS) * SBYTES);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma16(kb8, c0 * (D * 2) + koff[j], st + (w * LPW + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma16(vb8, c0 * 2 + voff[j], st + KBYTES + (w * LPW + j) * 1024);
+  };
+
+  f32x4 o[QT][NDT];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
+
+  auto compute = [&](int c) {
+    const int c0 = k0 + c * CK;
+    const int lim = min(k1, c0 + CK) - c0;   // valid keys of the chunk
+    const uint8_t* ks = lds + (c % NS) * SBYTES;
+    const uint8_t* vs = ks + KBYTES;
+#pragma unroll
+    for (int kb = 0; kb < CK; kb += 32) {   // one P.V step of 32 keys
+      // two S^T tiles: tile A rows -> keys kb + 8*(row/4) + row%4, tile B -> +4
+      const int rowA = kb + ((col >> 2) << 3) + (col & 3);
+      const int rowB = rowA + 4;
+      f32x4 sa[QT], sb[QT];
+#pragma unroll
+      for (int j = 0; j < QT; ++j) sa[j] = sb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < NFD; ++f) {
+        const int p = f * 4 + g4;
+        const u32x4 ka = *(const u32x4*)(ks + rowA * (D * 2) + ((p ^ kswz(rowA)) << 4));
+        const u32x4 kb2 = *(const u32x4*)(ks + rowB * (D * 2) + ((p ^ kswz(rowB)) << 4));
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+          sa[j] = E::mma(ka, qf[j][f], sa[j]);
+          sb[j] = E::mma(kb2, qf[j][f], sb[j]);
+        }
+      }
+      // lane holds keys c0 + kb + 8*g4 + e (e < 8) for query column `col`
+      u32x4 pf[QT];
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = sa[j][e];
+          sv[4 + e] = sb[j][e];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kk = kb + 8 * g4 + e;
+          sv[e] = (kk < lim && c0 + kk <= key_lim[j]) ? sv[e] * a.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sv[e]);
+        }
+        mx = wave_xor_max16_32(mx);
+        const float m_new = fmaxf(m_run[j], mx);
+        const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run[j] - m_safe);
+        float pv[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = exp2f(sv[e] - m_safe);
+          psum += pv[e];
+        }
+        l_run[j] = l_run[j] * alpha + psum;
+        m_run[j] = m_new;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
+        pf[j] = f_to_frag<T>(pv);
+      }
+      // V^T columns past the split end hold whatever the cache holds there:
+      // zero them so that 0 * V stays 0
+      const int vlim = lim - (kb + 8 * g4);   // valid keys of this lane's eight
+      uint32_t keep[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        keep[e2] = (2 * e2 + 1 < vlim) ? 0xFFFFFFFFu : (2 * e2 < vlim) ? 0x0000FFFFu : 0u;
+      const int p = (kb >> 3) + g4;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        const int dr = t * 16 + col;
+        u32x4 vf = *(const u32x4*)(vs + dr * (CK * 2) + ((p ^ vswz(dr)) << 4));
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) vf[e2] &= keep[e2];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) o[j][t] = E::mma(vf, pf[j], o[j][t]);
+      }
+    }
+  };
+
+  // Pipeline: chunks 0 .. NS-2 in flight; at chunk c wait for it (the loads
+  // of later chunks may stay outstanding), barrier (it is visible to every
+  // wave, and every wave is done with chunk c - 1), issue chunk c + NS - 1
+  // into the stage chunk c - 1 used, compute chunk c.
+  const int nchunks = (k1 - k0 + CK - 1) / CK;   // >= 1
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nchunks) issue(c);
+  for (int c = 0; c < nchunks; ++c) {
+    const int later = min(NS - 2, nchunks - 1 - c);   // chunks issued after c
+    static_assert(NS - 2 <= 3, "wait ladder");
+    if (later == 3) wait_vm<2 * LPW * 3>();
+    else if (later == 2) wait_vm<2 * LPW * 2>();
+    else if (later == 1) wait_vm<2 * LPW>();
+    else wait_vm<0>();
+    __syncthreads();
+    if (c + NS - 1 < nchunks) issue(c + NS - 1);
+    compute(c);
+  }
+  wait_vm<0>();   // (none outstanding: the last chunk waited for all)
+
+  const size_t wstride = (size_t)D * 16 + 32;
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    const float l_sum = wave_xor_sum16_32(l_run[j]);
+    if (qg[j] >= a.qgroups) continue;   // padding query group
+    const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg[j];
+    float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) *(f32x4*)(pp + (t * 64 + lane) * 4) = o[j][t];
+    if (g4 == 0) {
+      pp[D * 16 + col] = m_run[j];
+      pp[D * 16 + 16 + col] = l_sum;
+    }
   }
 }
 
@@ -416,20 +722,28 @@ static unsigned attn_grid(const AttnArgs& a, int qg_per_wg) {
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
-  // two query groups per workgroup (eight waves) whenever there are several:
-  // each staged K/V chunk then serves 128 query rows
-  const int QG = a_in.qgroups > 1 ? 2 : 1;
-  unsigned nblk = attn_grid(a, QG);   // a multiple of 8
+  // query groups per workgroup (see attn_groups_per_wg): one 4-wave group,
+  // two (eight waves), or four (eight waves of two query tiles each)
+  const int GPW = attn_groups_per_wg((int)sizeof(T), a_in.qgroups);
+  unsigned nblk = attn_grid(a, GPW);   // a multiple of 8
   if (a.warm.w) {
     a.warm.first = (int)nblk;
     nblk += (unsigned)a.warm.consumers;
   }
   dim3 grid(nblk);
-  switch (a.d * 4 + QG) {
-    case 64 * 4 + 1: hipLaunchKernelGGL((attention_kernel<T, 64, 1>), grid, dim3(256), 0, s, a); break;
-    case 64 * 4 + 2: hipLaunchKernelGGL((attention_kernel<T, 64, 2>), grid, dim3(512), 0, s, a); break;
-    case 128 * 4 + 1: hipLaunchKernelGGL((attention_kernel<T, 128, 1>), grid, dim3(256), 0, s, a); break;
-    case 128 * 4 + 2: hipLaunchKernelGGL((attention_kernel<T, 128, 2>), grid, dim3(512), 0, s, a); break;
+  switch (a.d * 8 + GPW) {
+    case 64 * 8 + 1: hipLaunchKernelGGL((attention_kernel<T, 64, 1, 1>), grid, dim3(256), 0, s, a); break;
+    case 64 * 8 + 2: hipLaunchKernelGGL((attention_kernel<T, 64, 2, 1>), grid, dim3(512), 0, s, a); break;
+    case 128 * 8 + 1: hipLaunchKernelGGL((attention_kernel<T, 128, 1, 1>), grid, dim3(256), 0, s, a); break;
+    case 128 * 8 + 2: hipLaunchKernelGGL((attention_kernel<T, 128, 2, 1>), grid, dim3(512), 0, s, a); break;
+    case 64 * 8 + 4:
+      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((attention_kernel<T, 64, 2, 2>), grid, dim3(512), 0, s, a);
+      else return hipErrorInvalidValue;
+      break;
+    case 128 * 8 + 4:
+      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL(attention_mq_kernel, grid, dim3(512), 0, s, a);
+      else return hipErrorInvalidValue;
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -186,6 +186,12 @@ __host__ __device__ inline void attn_split_counts(const AttnArgs& a, int ctx_len
   }
 }
 size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d);
+// Query groups (64 query rows each) per attention workgroup: one (four
+// waves), two (eight waves), or, for 2-byte operands and at least four
+// groups, four (eight waves of two query tiles each).
+inline int attn_groups_per_wg(int elem_bytes, int qgroups) {
+  return qgroups >= 4 && elem_bytes == 2 ? 4 : qgroups > 1 ? 2 : 1;
+}
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Merge attention splits in index order; write o (frag layout over nq*d).
