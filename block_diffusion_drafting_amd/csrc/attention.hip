@@ -625,17 +625,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
 }
 
-// One workgroup per (sequence, KV head, query group, 16-row d-tile), 16
-// waves: wave w handles query tile 4*qg + w%4 over the quarter w/4 of the
-// splits (its loads all issued at once), then the quarters are merged in
-// order through LDS.  Writes its part of o (frag layout of the model type T
-// over nq*d, input of the output projection).
-template <typename T, int D>
-__global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out) {
+// One workgroup per (sequence, KV head, query group, 16-row d-tile) with 4 Q
+// waves: wave w handles query tile 4*qg + w%4 over the part w/4 of Q of the
+// splits (its loads all issued in batches of eight), then the parts are
+// merged in order through LDS.  Q = 4 when there are many splits, 1 (four
+// waves, no LDS merge) when there are at most eight.  Writes its part of o
+// (frag layout of the model type T over nq*d, input of the output
+// projection).
+template <typename T, int D, int Q>
+__global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag out) {
   constexpr int NDT = D / 16;
   constexpr int BATCH = 8;
-  __shared__ float sm[4][4][64], sl[4][4][64];
-  __shared__ f32x4 so[4][4][64];
+  __shared__ float sm[Q][4][64], sl[Q][4][64];
+  __shared__ f32x4 so[Q][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qt = wave & 3, quarter = wave >> 2;
   const int g4 = lane >> 4, col = lane & 15;
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out
   const int ctx_len = a.seqs[b].ctx_len;
   int n_cs, n_s;
   attn_split_counts(a, ctx_len, n_cs, n_s);
-  const int per = (n_s + 3) / 4;
+  const int per = (n_s + Q - 1) / Q;
   const int s_begin = min(n_s, quarter * per), s_end = min(n_s, s_begin + per);
   const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
   const size_t wstride = (size_t)D * 16 + 32;
@@ -684,24 +686,26 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(AttnArgs a, Frag out
       M = Mn;
     }
   }
-  sm[quarter][qt][lane] = M;
-  sl[quarter][qt][lane] = L;
-  so[quarter][qt][lane] = o;
-  __syncthreads();
-  if (quarter != 0) return;
-  M = -INFINITY;
-  L = 0.f;
-  o = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (Q > 1) {
+    sm[quarter][qt][lane] = M;
+    sl[quarter][qt][lane] = L;
+    so[quarter][qt][lane] = o;
+    __syncthreads();
+    if (quarter != 0) return;
+    M = -INFINITY;
+    L = 0.f;
+    o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float mk = sm[k][qt][lane];
-    if (mk == -INFINITY) continue;
-    const float Mn = fmaxf(M, mk);
-    const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
-    const float a1 = exp2f(mk - Mn);
-    L = L * a0 + sl[k][qt][lane] * a1;
-    o = o * a0 + so[k][qt][lane] * a1;
-    M = Mn;
+    for (int k = 0; k < Q; ++k) {
+      const float mk = sm[k][qt][lane];
+      if (mk == -INFINITY) continue;
+      const float Mn = fmaxf(M, mk);
+      const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+      const float a1 = exp2f(mk - Mn);
+      L = L * a0 + sl[k][qt][lane] * a1;
+      o = o * a0 + so[k][qt][lane] * a1;
+      M = Mn;
+    }
   }
   const int rep = a.nq / a.nkv;
   const int r = (qg * 4 + qt) * 16 + col;
@@ -755,9 +759,12 @@ template hipError_t launch_attention<float>(const AttnArgs&, hipStream_t);
 template <typename CT, typename T>
 hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s) {
   dim3 grid((unsigned)a.B * a.nkv * a.qgroups * (a.d / 16));
-  switch (a.d) {
-    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), grid, dim3(1024), 0, s, a, o); break;
-    case 128: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), grid, dim3(1024), 0, s, a, o); break;
+  const bool few = a.max_splits <= 8;   // one part: four waves per workgroup
+  switch (a.d * 2 + (few ? 1 : 0)) {
+    case 64 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 4>), grid, dim3(1024), 0, s, a, o); break;
+    case 64 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 1>), grid, dim3(256), 0, s, a, o); break;
+    case 128 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4>), grid, dim3(1024), 0, s, a, o); break;
+    case 128 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1>), grid, dim3(256), 0, s, a, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
