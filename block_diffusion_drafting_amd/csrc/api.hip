@@ -512,7 +512,7 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
   c->warm_qkv = env_int("DFLASH_WARM_QKV", c->warm_qkv, 0, 64);
   c->warm_lm = env_int("DFLASH_WARM_LM", c->warm_lm, 0, 64);
   c->attn_wgs_per_cu = env_int("DFLASH_ATTN_WGS_PER_CU", c->attn_wgs_per_cu, 1, 16);
-  c->attn_min_split = round_up(env_int("DFLASH_ATTN_MIN_SPLIT", c->attn_min_split, 128, 1 << 20), 64);
+  c->attn_min_split = round_up(env_int("DFLASH_ATTN_MIN_SPLIT", c->attn_min_split, 64, 1 << 20), 64);
   c->seq_dev = (DevSeq*)c->alloc.get(sizeof(DevSeq) * batch);
   if (!c->seq_dev) {
     delete c;
