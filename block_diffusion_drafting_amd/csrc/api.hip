@@ -1098,7 +1098,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   {
     PhaseTimer tm(c, PH_FINAL, s);
     HIP_TRY(launch_finalize<T>((const unsigned long long*)c->keys.p, M, draft, (const float*)c->x.p,
-                               (const float*)c->ssq.p, G, m->final_gain(), H, (float)cf.rms_eps, hidden, s));
+                               (const float*)c->ssq.p, e.ssq_groups, m->final_gain(), H, (float)cf.rms_eps, hidden, s));
   }
   return DFLASH_OK;
 }
