@@ -540,8 +540,198 @@ inline hipError_t launch_fixed(const GemmPlan& p, const GemmArgs& g, const EpiAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// LM head over 128-row m-groups (bf16 model, activations without the lo
+// part): the waves of a workgroup split its tiles (up to NTW each, the whole
+// reduction each), so one copy of each activation fragment, staged in LDS,
+// feeds every wave; in the k-split form above, every workgroup of five
+// tiles re-reads the whole activation from L2 and each wave keeps one load
+// batch in flight.  Stages of KC k-blocks x 8 m-tiles (16 KiB) are double
+// buffered; the next stage's activation and weight loads are in flight
+// while the current one is computed, and the last stage is peeled so that
+// every load in the loop is unconditional (a weight tile past the wave's
+// range re-reads its last tile, never used; activation k-blocks past the
+// end are zero).  The epilogue is the argmax epilogue of gemm_kernel, per
+// tile, on complete sums.
+// ---------------------------------------------------------------------------
+constexpr int HEAD_WAVES = 8;
+constexpr int HEAD_NTW = 3;   // tiles per wave at most
+constexpr int HEAD_KC = 2;    // k-blocks per stage
+
+template <typename T>
+__global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel(GemmArgs g,
+                                                                                                  EpiArgs e) {
+  using E = Elem<T>;
+  constexpr int MTT = 8, NTW = HEAD_NTW, KC = HEAD_KC, NTH = HEAD_WAVES * 64;
+  constexpr int XPT = KC * MTT * WAVE / NTH;   // activation fragments staged per thread
+  static_assert(XPT * NTH == KC * MTT * WAVE, "stage");
+  __shared__ u32x4 xs[2][KC][MTT][WAVE];
+  __shared__ unsigned long long kmax[MTT][16];
+  __shared__ float rnorm[MTT * 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // unit (tile group) and m-group, numbered as in gemm_kernel
+  int ng, mg;
+  if (g.m_groups > 1) {
+    const int q = (int)(blockIdx.x >> 3);
+    ng = (q / g.m_groups) * 8 + (int)(blockIdx.x & 7);
+    if (ng >= g.n_groups) return;
+    mg = q % g.m_groups;
+  } else {
+    ng = blockIdx.x;
+    mg = 0;
+  }
+  const int tile0 = (int)((long)ng * g.W.n_tiles / g.n_groups);
+  const int nt = (int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0;
+  const int ntw = (nt + HEAD_WAVES - 1) / HEAD_WAVES;              // <= NTW (checked at launch)
+  const int wt0 = tile0 + wave * ntw;
+  const int wnt = __builtin_amdgcn_readfirstlane(max(0, min(ntw, tile0 + nt - wt0)));
+  const int mt0 = mg * MTT;
+  const int nkb = g.W.nkb;
+
+  const uint8_t* wb[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int tile = wnt > 0 ? wt0 + min(t, wnt - 1) : tile0;
+    wb[t] = g.W.w + (size_t)tile * nkb * BLOCK_BYTES + lane * FRAG_BYTES;
+  }
+  f32x4 acc[NTW][MTT];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // norm scale of the 128 rows: thread (part p, row r) adds groups p, p + P, ...
+  {
+    constexpr int R = MTT * 16, P = NTH / R;
+    __shared__ float npart[P][R];
+    const int r = threadIdx.x % R, part = threadIdx.x / R;
+    const int m = mt0 * 16 + r;
+    float sum = 0.f;
+    if (m < e.M)
+      for (int q = part; q < e.ssq_groups; q += P) sum += e.ssq[(size_t)q * e.M + m];
+    npart[part][r] = sum;
+    if (threadIdx.x < MTT * 16) (&kmax[0][0])[threadIdx.x] = 0ull;
+    __syncthreads();
+    if (threadIdx.x < R) {
+      float tt = 0.f;
+#pragma unroll
+      for (int q = 0; q < P; ++q) tt += npart[q][threadIdx.x];
+      rnorm[threadIdx.x] = m < e.M ? rsqrtf(tt / (float)e.norm_dim + e.eps) : 0.f;
+    }
+  }
+
+  struct Stage {
+    u32x4 x[XPT];
+    u32x4 w[NTW][KC];
+  };
+  // stage s: k-blocks s*KC .. s*KC+KC-1 (past nkb: activation zero, weight
+  // address clamped to the last k-block)
+  auto load = [&](Stage& st, int s) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = threadIdx.x + j * NTH;
+      const int kbi = i / (MTT * WAVE), mt = (i / WAVE) % MTT, ln = i % WAVE;
+      const int kb = s * KC + kbi;
+      const bool ok = kb < nkb && mt0 + mt < g.X.mtiles;
+      const size_t slot = ((size_t)min(mt0 + mt, g.X.mtiles - 1) * g.X.nkb + min(kb, nkb - 1)) * WAVE + ln;
+      const u32x4 v = g.X.hi[slot];
+      st.x[j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int kb = min(s * KC + k, nkb - 1);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        st.w[t][k] = __builtin_nontemporal_load((const u32x4*)(wb[t] + (size_t)kb * BLOCK_BYTES));
+    }
+  };
+  auto stash = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int i = threadIdx.x + j * NTH;
+      (&xs[buf][0][0][0])[i] = st.x[j];
+    }
+  };
+  auto compute = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      u32x4 xf[MTT];
+#pragma unroll
+      for (int mt = 0; mt < MTT; ++mt) xf[mt] = xs[buf][k][mt][lane];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        if (t >= wnt) continue;   // uniform over the wave
+#pragma unroll
+        for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = E::mma(st.w[t][k], xf[mt], acc[t][mt]);
+      }
+    }
+  };
+
+  const int nst = (nkb + KC - 1) / KC;
+  Stage a, b;
+  load(a, 0);
+  stash(a, 0);
+  __syncthreads();
+  int s = 0;
+  for (; s + 1 < nst; ++s) {
+    load(b, s + 1);
+    compute(a, s & 1);
+    stash(b, (s + 1) & 1);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int k = 0; k < KC; ++k) a.w[t][k] = b.w[t][k];
+    __syncthreads();
+  }
+  compute(a, s & 1);
+
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    if (t >= wnt) continue;
+#pragma unroll
+    for (int mt = 0; mt < MTT; ++mt)
+      epilogue_tile<T, EPI_ARGMAX>(e, 0, wt0 + t, mt0 + mt, acc[t][mt], lane, rnorm[mt * 16 + (lane & 15)],
+                                   kmax[mt]);
+  }
+  __syncthreads();
+  if (threadIdx.x < MTT * 16) {
+    const int m = (mt0 + threadIdx.x / 16) * 16 + (threadIdx.x & 15);
+    const unsigned long long k = (&kmax[0][0])[threadIdx.x];
+    if (m < e.M && k) atomicMax(e.keys + m, k);
+  }
+}
+
+// Tile groups of the head kernel: about two rounds of 256 workgroups, at
+// most HEAD_WAVES * HEAD_NTW tiles each.
+inline int head_groups(int n_tiles) {
+  const int cap = HEAD_WAVES * HEAD_NTW;
+  int G = n_tiles < 512 ? n_tiles : 512;
+  if ((n_tiles + G - 1) / G > cap) G = (n_tiles + cap - 1) / cap;
+  return G;
+}
+
+template <typename T>
+inline hipError_t launch_head(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  g.n_groups = head_groups(g.W.n_tiles);
+  g.m_groups = p.m_groups;
+  g.nsplit = 1;
+  g.kbu = g.W.nkb;
+  if ((g.W.n_tiles + g.n_groups - 1) / g.n_groups > HEAD_WAVES * HEAD_NTW || g.X.nkb < g.W.nkb ||
+      g.X.mtiles < 1)
+    return hipErrorInvalidValue;
+  const unsigned units = (unsigned)g.n_groups;
+  dim3 grid(p.m_groups > 1 ? (units + 7u) / 8u * 8u * (unsigned)p.m_groups : units);
+  hipLaunchKernelGGL((head_kernel<T>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
+  return hipGetLastError();
+}
+
 template <typename T, int EPI>
 hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  if constexpr (EPI == EPI_ARGMAX && sizeof(T) == 2) {
+    if (uses_head_kernel(EPI, p, (int)sizeof(T))) return launch_head<T>(p, g, e, s);
+  }
   g.kbu = p.kbu;
   g.nsplit = p.nsplit;
   g.n_groups = p.n_groups;
