@@ -268,9 +268,17 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
           mx = fmaxf(mx, sv[j][e]);
         }
         mx = wave_xor_max16_32(mx);
-        const float m_new = fmaxf(m_run[j], mx);
-        const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run[j] - m_safe);
+        // lazy rescaling (as in attention_mq_kernel): the reference moves
+        // only when a column's maximum exceeds it by more than 8 (log2 units)
+        if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
+          const float m_new = fmaxf(m_run[j], mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[j] - m_new);
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
+          m_run[j] = m_new;
+        }
+        const float m_safe = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
         float pv[8];
         float psum = 0.f;
 #pragma unroll
@@ -280,10 +288,7 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
             psum += pv[e];
           }
         }
-        l_run[j] = l_run[j] * alpha + psum;
-        m_run[j] = m_new;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
+        l_run[j] += psum;
         pf[j] = f_to_frag<T>(pv);
       }
 #pragma unroll
@@ -552,9 +557,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           mx = fmaxf(mx, sv[e]);
         }
         mx = wave_xor_max16_32(mx);
-        const float m_new = fmaxf(m_run[j], mx);
-        const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run[j] - m_safe);
+        // Lazy rescaling: the reference m_run moves (and O and l are
+        // rescaled) only when some column's maximum exceeds it by more than
+        // 8 (log2 units), so exponentials stay below 2^8 (safe in fp32 and
+        // as fp16 probabilities) and the rescaling, which costs more VALU
+        // work than the rest of the step, is skipped once the maxima settle.
+        // O / l is the same for any reference; the merge of the splits
+        // takes (m, l, O) with any reference.
+        if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
+          const float m_new = fmaxf(m_run[j], mx);
+          const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[j] - m_new);
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
+          m_run[j] = m_new;
+        }
+        const float m_safe = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
         float pv[8];
         float psum = 0.f;
 #pragma unroll
@@ -562,10 +580,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           pv[e] = exp2f(sv[e] - m_safe);
           psum += pv[e];
         }
-        l_run[j] = l_run[j] * alpha + psum;
-        m_run[j] = m_new;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
+        l_run[j] += psum;
         pf[j] = f_to_frag<T>(pv);
       }
       // V^T columns past the split end hold whatever the cache holds there:
