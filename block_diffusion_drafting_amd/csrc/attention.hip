@@ -261,18 +261,29 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int j = 0; j < QT; ++j) {
         float mx = -INFINITY;
+        // every key of the chunk valid and visible to every query of the
+        // wave (wave-uniform): no per-element mask
+        if (cend - c0 == CHUNK_KEYS && __ballot(c0 + CHUNK_KEYS - 1 > key_lim[j]) == 0ull) {
 #pragma unroll
-        for (int e = 0; e < NV; ++e) {
-          const int key = c0 + kb + g4 * NV + e;
-          sv[j][e] = (key < cend && key <= key_lim[j]) ? sv[j][e] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sv[j][e]);
+          for (int e = 0; e < NV; ++e) {
+            sv[j][e] *= a.scale_log2;
+            mx = fmaxf(mx, sv[j][e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < NV; ++e) {
+            const int key = c0 + kb + g4 * NV + e;
+            sv[j][e] = (key < cend && key <= key_lim[j]) ? sv[j][e] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[j][e]);
+          }
         }
         mx = wave_xor_max16_32(mx);
-        // lazy rescaling (as in attention_mq_kernel): the reference moves
-        // only when a column's maximum exceeds it by more than 8 (log2 units)
+        // lazy rescaling and the hardware 2^x (as in attention_mq_kernel):
+        // the reference moves only when a column's maximum exceeds it by
+        // more than 8 (log2 units)
         if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
           const float m_new = fmaxf(m_run[j], mx);
-          const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[j] - m_new);
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
           l_run[j] *= alpha;
 #pragma unroll
           for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
@@ -284,7 +295,7 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (e < NV) {
-            pv[e] = exp2f(sv[j][e] - m_safe);
+            pv[e] = __builtin_amdgcn_exp2f(sv[j][e] - m_safe);
             psum += pv[e];
           }
         }
@@ -550,11 +561,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           sv[4 + e] = sb[j][e];
         }
         float mx = -INFINITY;
+        // every key of the chunk valid and visible to every query of the
+        // wave (wave-uniform): no per-element mask
+        if (lim == CK && __ballot(c0 + CK - 1 > key_lim[j]) == 0ull) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kk = kb + 8 * g4 + e;
-          sv[e] = (kk < lim && c0 + kk <= key_lim[j]) ? sv[e] * a.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sv[e]);
+          for (int e = 0; e < 8; ++e) {
+            sv[e] *= a.scale_log2;
+            mx = fmaxf(mx, sv[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kk = kb + 8 * g4 + e;
+            sv[e] = (kk < lim && c0 + kk <= key_lim[j]) ? sv[e] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[e]);
+          }
         }
         mx = wave_xor_max16_32(mx);
         // Lazy rescaling: the reference m_run moves (and O and l are
@@ -566,18 +587,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         // takes (m, l, O) with any reference.
         if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
           const float m_new = fmaxf(m_run[j], mx);
-          const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[j] - m_new);
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
           l_run[j] *= alpha;
 #pragma unroll
           for (int t = 0; t < NDT; ++t) o[j][t] *= alpha;
           m_run[j] = m_new;
         }
+        // (the hardware 2^x: arguments lie in [-inf, 8], and a result it
+        // flushes below 2^-126 is negligible beside the column's largest
+        // probability, which is at least 1)
         const float m_safe = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
         float pv[8];
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2f(sv[e] - m_safe);
+          pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_safe);
           psum += pv[e];
         }
         l_run[j] += psum;
