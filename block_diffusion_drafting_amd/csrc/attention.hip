@@ -550,7 +550,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           sb[j] = E::mma(kb2, qf[j][f], sb[j]);
         }
       }
-      // lane holds keys c0 + kb + 8*g4 + e (e < 8) for query column `col`
+      // lane holds keys c0 + kb + 8*g4 + e (e < 8) for query column `col`.
+      // Maxima are taken on the raw scores (the scale is positive) and the
+      // scale is folded into the exponent: p = 2^(s * scale - m).
+      const float sc = a.scale_log2;
       u32x4 pf[QT];
 #pragma unroll
       for (int j = 0; j < QT; ++j) {
@@ -560,24 +563,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
           sv[e] = sa[j][e];
           sv[4 + e] = sb[j][e];
         }
-        float mx = -INFINITY;
         // every key of the chunk valid and visible to every query of the
         // wave (wave-uniform): no per-element mask
-        if (lim == CK && __ballot(c0 + CK - 1 > key_lim[j]) == 0ull) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            sv[e] *= a.scale_log2;
-            mx = fmaxf(mx, sv[e]);
-          }
-        } else {
+        if (!(lim == CK && __ballot(c0 + CK - 1 > key_lim[j]) == 0ull)) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kk = kb + 8 * g4 + e;
-            sv[e] = (kk < lim && c0 + kk <= key_lim[j]) ? sv[e] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[e]);
+            sv[e] = (kk < lim && c0 + kk <= key_lim[j]) ? sv[e] : -INFINITY;
           }
         }
-        mx = wave_xor_max16_32(mx);
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = wave_xor_max16_32(mx) * sc;
         // Lazy rescaling: the reference m_run moves (and O and l are
         // rescaled) only when some column's maximum exceeds it by more than
         // 8 (log2 units), so exponentials stay below 2^8 (safe in fp32 and
@@ -601,28 +597,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_safe);
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], sc, -m_safe));
           psum += pv[e];
         }
         l_run[j] += psum;
-        pf[j] = f_to_frag<T>(pv);
+        // probabilities lie in [0, 2^8]: round to fp16 without the clamp
+        const f16x8 ph = {(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3],
+                          (_Float16)pv[4], (_Float16)pv[5], (_Float16)pv[6], (_Float16)pv[7]};
+        pf[j] = __builtin_bit_cast(u32x4, ph);
       }
-      // V^T columns past the split end hold whatever the cache holds there:
-      // zero them so that 0 * V stays 0
-      const int vlim = lim - (kb + 8 * g4);   // valid keys of this lane's eight
-      uint32_t keep[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        keep[e2] = (2 * e2 + 1 < vlim) ? 0xFFFFFFFFu : (2 * e2 < vlim) ? 0x0000FFFFu : 0u;
       const int p = (kb >> 3) + g4;
+      if (lim == CK) {   // (uniform)
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        const int dr = t * 16 + col;
-        u32x4 vf = *(const u32x4*)(vs + dr * (CK * 2) + ((p ^ vswz(dr)) << 4));
+        for (int t = 0; t < NDT; ++t) {
+          const int dr = t * 16 + col;
+          const u32x4 vf = *(const u32x4*)(vs + dr * (CK * 2) + ((p ^ vswz(dr)) << 4));
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) vf[e2] &= keep[e2];
+          for (int j = 0; j < QT; ++j) o[j][t] = E::mma(vf, pf[j], o[j][t]);
+        }
+      } else {
+        // V^T columns past the split end hold whatever the cache holds
+        // there: zero them so that 0 * V stays 0
+        const int vlim = lim - (kb + 8 * g4);   // valid keys of this lane's eight
+        uint32_t keep[4];
 #pragma unroll
-        for (int j = 0; j < QT; ++j) o[j][t] = E::mma(vf, pf[j], o[j][t]);
+        for (int e2 = 0; e2 < 4; ++e2)
+          keep[e2] = (2 * e2 + 1 < vlim) ? 0xFFFFFFFFu : (2 * e2 < vlim) ? 0x0000FFFFu : 0u;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          const int dr = t * 16 + col;
+          u32x4 vf = *(const u32x4*)(vs + dr * (CK * 2) + ((p ^ vswz(dr)) << 4));
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) vf[e2] &= keep[e2];
+#pragma unroll
+          for (int j = 0; j < QT; ++j) o[j][t] = E::mma(vf, pf[j], o[j][t]);
+        }
       }
     }
   };
