@@ -256,28 +256,26 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[j][e] = sa[j][e];
       }
-      // lane holds keys c0 + kb + g4*NV + e for query column `col`
+      // lane holds keys c0 + kb + g4*NV + e for query column `col`; maxima
+      // on the raw scores, the scale folded into the exponent (as in
+      // attention_mq_kernel)
+      const float sc = a.scale_log2;
       u32x4 pf[QT];
 #pragma unroll
       for (int j = 0; j < QT; ++j) {
-        float mx = -INFINITY;
         // every key of the chunk valid and visible to every query of the
         // wave (wave-uniform): no per-element mask
-        if (cend - c0 == CHUNK_KEYS && __ballot(c0 + CHUNK_KEYS - 1 > key_lim[j]) == 0ull) {
-#pragma unroll
-          for (int e = 0; e < NV; ++e) {
-            sv[j][e] *= a.scale_log2;
-            mx = fmaxf(mx, sv[j][e]);
-          }
-        } else {
+        if (!(cend - c0 == CHUNK_KEYS && __ballot(c0 + CHUNK_KEYS - 1 > key_lim[j]) == 0ull)) {
 #pragma unroll
           for (int e = 0; e < NV; ++e) {
             const int key = c0 + kb + g4 * NV + e;
-            sv[j][e] = (key < cend && key <= key_lim[j]) ? sv[j][e] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[j][e]);
+            sv[j][e] = (key < cend && key <= key_lim[j]) ? sv[j][e] : -INFINITY;
           }
         }
-        mx = wave_xor_max16_32(mx);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) mx = fmaxf(mx, sv[j][e]);
+        mx = wave_xor_max16_32(mx) * sc;
         // lazy rescaling and the hardware 2^x (as in attention_mq_kernel):
         // the reference moves only when a column's maximum exceeds it by
         // more than 8 (log2 units)
@@ -295,12 +293,19 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (e < NV) {
-            pv[e] = __builtin_amdgcn_exp2f(sv[j][e] - m_safe);
+            pv[e] = __builtin_amdgcn_exp2f(fmaf(sv[j][e], sc, -m_safe));
             psum += pv[e];
           }
         }
         l_run[j] += psum;
-        pf[j] = f_to_frag<T>(pv);
+        if constexpr (ES == 2) {
+          // probabilities lie in [0, 2^8]: round to fp16 without the clamp
+          const f16x8 ph = {(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3],
+                            (_Float16)pv[4], (_Float16)pv[5], (_Float16)pv[6], (_Float16)pv[7]};
+          pf[j] = __builtin_bit_cast(u32x4, ph);
+        } else {
+          pf[j] = f_to_frag<T>(pv);
+        }
       }
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
