@@ -611,8 +611,8 @@ def bench_adaptive(args, torch, dfl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
-                                   "note, not implemented", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this library runs on one GPU only; sharding across GPUs is not "
+                                   "implemented", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import block_diffusion_drafting_amd as dfl

@@ -16,7 +16,7 @@ Sources (page title, section):
   [G-PRED]  same post, "Predictability": acceptance decays along the block,
             slowly for math and code, quickly for chat.
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
   * acceptance model: position i of a block agrees with probability
     p_i = a * gamma^i, independently; tau = 1 + the leading run of
     agreements (the extra one is the target's own token);

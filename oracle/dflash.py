@@ -19,7 +19,7 @@ Sources (page title, section):
   [G-AR]    same post, "Overcoming the autoregressive bottleneck".
   [G-BENCH] same post, table 2 caption (greedy decoding).
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
   * block row i sits at position ctx_len + i; its argmax is the draft for
     position ctx_len + 1 + i, so all K rows are drafts and the acceptance
     length is in [1, K + 1];

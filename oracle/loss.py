@@ -15,7 +15,7 @@ Sources (page title, section):
             gamma^k, so earlier positions weigh more (an early error voids the
             rest of the block).
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
   * block row k (k = 0 .. K-1) predicts the response token at anchor + 1 + k
     (the same shift as the draft block: row i proposes position ctx_len+1+i)
     and carries weight gamma^k; rows past the response end are ignored;

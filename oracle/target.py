@@ -21,7 +21,7 @@ Sources (page title, section):
             3.5x", "System architecture": hidden states of several target
             layers, concatenated, are the drafter's context features.
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
   * the target is a decoder of the same layer form as the drafter (RMSNorm,
     GQA attention with rotate-half RoPE, SwiGLU MLP, final RMSNorm, LM head)
     but causal: block row i sees the committed positions and block rows
