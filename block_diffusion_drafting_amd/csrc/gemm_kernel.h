@@ -541,12 +541,12 @@ inline hipError_t launch_fixed(const GemmPlan& p, const GemmArgs& g, const EpiAr
 }
 
 // ---------------------------------------------------------------------------
-// LM head over 128-row m-groups (bf16 model, activations without the lo
-// part): the waves of a workgroup split its tiles (up to NTW each, the whole
+// LM head over m-groups of MTT = 8 or 4 m-tiles (128 or 64 rows; bf16
+// model, activations without the lo part): the waves of a workgroup split its tiles (up to NTW each, the whole
 // reduction each), so one copy of each activation fragment, staged in LDS,
 // feeds every wave; in the k-split form above, every workgroup of five
 // tiles re-reads the whole activation from L2 and each wave keeps one load
-// batch in flight.  Stages of KC k-blocks x 8 m-tiles (16 KiB) are double
+// batch in flight.  Stages of KC k-blocks x MTT m-tiles are double
 // buffered; the next stage's activation and weight loads are in flight
 // while the current one is computed, and the last stage is peeled so that
 // every load in the loop is unconditional (a weight tile past the wave's
@@ -558,11 +558,11 @@ constexpr int HEAD_WAVES = 8;
 constexpr int HEAD_NTW = 3;   // tiles per wave at most
 constexpr int HEAD_KC = 2;    // k-blocks per stage
 
-template <typename T>
+template <typename T, int MTT>
 __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel(GemmArgs g,
                                                                                                   EpiArgs e) {
   using E = Elem<T>;
-  constexpr int MTT = 8, NTW = HEAD_NTW, KC = HEAD_KC, NTH = HEAD_WAVES * 64;
+  constexpr int NTW = HEAD_NTW, KC = HEAD_KC, NTH = HEAD_WAVES * 64;
   constexpr int XPT = KC * MTT * WAVE / NTH;   // activation fragments staged per thread
   static_assert(XPT * NTH == KC * MTT * WAVE, "stage");
   __shared__ u32x4 xs[2][KC][MTT][WAVE];
@@ -723,7 +723,9 @@ inline hipError_t launch_head(const GemmPlan& p, GemmArgs g, const EpiArgs& e, h
     return hipErrorInvalidValue;
   const unsigned units = (unsigned)g.n_groups;
   dim3 grid(p.m_groups > 1 ? (units + 7u) / 8u * 8u * (unsigned)p.m_groups : units);
-  hipLaunchKernelGGL((head_kernel<T>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
+  if (p.mtt == 8) hipLaunchKernelGGL((head_kernel<T, 8>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
+  else if (p.mtt == 4) hipLaunchKernelGGL((head_kernel<T, 4>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -112,11 +112,12 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor);
 
-// The LM head of a bf16 model over 128-row m-groups (activations without
-// the lo part) runs head_kernel, whose waves split the tiles and share the
-// activations through LDS, instead of the k-split product kernel.
+// The LM head of a bf16 model over m-groups of 8 or 4 m-tiles (activations
+// without the lo part) runs head_kernel, whose waves split the tiles and
+// share the activations through LDS, instead of the k-split product kernel.
 inline bool uses_head_kernel(int epi, const GemmPlan& p, int elem_bytes) {
-  return epi == EPI_ARGMAX && elem_bytes == 2 && p.mtt == 8 && !p.split && !p.rowmajor && !p.fixed;
+  return epi == EPI_ARGMAX && elem_bytes == 2 && (p.mtt == 8 || p.mtt == 4) && !p.split && !p.rowmajor &&
+         !p.fixed;
 }
 
 template <typename T>
