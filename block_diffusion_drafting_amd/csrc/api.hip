@@ -138,8 +138,12 @@ struct dflash_ctx {
   Buf x, ssq, q, bk, bvt, keys, part, attn_part, rowmap;
   Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
   // L2 warm-up by the spare blocks of latency-bound kernels (fragments per
-  // product wave): output projection, next QKV, LM head
-  int warm_o = 16, warm_qkv = 12, warm_lm = 2;
+  // product wave): output projection, next QKV, LM head.  Measured on the
+  // Qwen3-4B-shaped K = 16 step: the output projection's warm-up pays (its
+  // whole weight set, from the attention kernel); those of the next QKV and
+  // of the LM head (from the residual pass) now cost the residual pass more
+  // than they save, so they are off by default.
+  int warm_o = 16, warm_qkv = 0, warm_lm = 0;
   // attention grid: 8-wave workgroup equivalents per compute unit, and the
   // shortest key split (a multiple of 64)
   int attn_wgs_per_cu = 2;
