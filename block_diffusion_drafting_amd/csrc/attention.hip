@@ -8,17 +8,23 @@
 // from the sequence's static cache, block K/V from this layer's QKV
 // epilogue.
 //
-// Work unit (one 256-thread workgroup): sequence b, KV head g, a group of up
-// to four 16-row query tiles (rows = block position x query head sharing g),
-// and one split of the key range (its partial result goes to a buffer that
+// Work unit: sequence b, KV head g, one to four query groups of up to four
+// 16-row query tiles (rows = block position x query head sharing g), and
+// one split of the key range (its partial result goes to a buffer that
 // attn_combine merges in split order).  A split is a run of 64-key chunks;
-// each chunk is staged in LDS once (K row-major, V transposed, padded rows
-// against bank conflicts) and read by all four waves, and the global loads
-// of the next chunk are in flight while the current one is computed.  S^T = K Q^T and O^T += V^T P^T run on MFMA; the
-// softmax is online per wave in fp32 (exp2 with the log2(e) folded into
-// the scale).  For bf16 the two 16-key S^T tiles of a 32-key step hold keys
-// in the order that makes each lane's probabilities the B-fragment of the
-// P.V product directly.
+// each chunk is staged in LDS once and read by every wave of the workgroup,
+// and the loads of the next chunks are in flight while the current one is
+// computed.  attention_kernel stages chunks through two register sets into
+// padded LDS rows (one 4-wave query group, two groups on 8 waves, or four
+// groups on 8 waves of two query tiles each at head_dim 64);
+// attention_mq_kernel (fp16, head_dim 128, at least four query groups)
+// loads them straight into four LDS stages, its waves carrying two query
+// tiles each.  S^T = K Q^T and O^T += V^T P^T run on MFMA; the softmax is
+// online per query column in fp32, with the scale and log2(e) folded into
+// the exponent of the hardware 2^x and the rescaling of O done lazily.  For
+// 2-byte operands the two 16-key S^T tiles of a 32-key step hold keys in
+// the order that makes each lane's probabilities the B-fragment of the P.V
+// product directly.
 //
 // Causal form (block verification, Google Developers Blog "Overcoming the
 // autoregressive bottleneck"): the QKV product has already stored the block
