@@ -47,12 +47,18 @@ size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d) {
   return (size_t)B * nkv * qgroups * max_splits * 4 * (d * 16 + 32);
 }
 
+// 16-byte nontemporal (streaming) global load.
+__device__ __forceinline__ u32x4 gld16_nt(const void* p) { return __builtin_nontemporal_load((gu32x4*)p); }
+
 // Two waves per SIMD (two 4-wave or one 8-wave workgroup per compute unit,
 // as the grid is planned): at most 256 registers per wave.  QG: 4-wave
 // groups of the workgroup (1 or 2); QT: query tiles per wave (1 or 2).  A
 // workgroup serves QG * QT query groups of 64 rows, and with QT = 2 every K
-// or V^T fragment read from LDS feeds two MFMAs.
-template <typename T, int D, int QG, int QT>
+// or V^T fragment read from LDS feeds two MFMAs.  NT: K/V chunks are loaded
+// nontemporally (the context K/V of a block too large to stay in the caches
+// between blocks; otherwise the default policy lets it stay there, as the
+// weights stream nontemporally).
+template <typename T, int D, int QG, int QT, bool NT>
 __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnArgs a) {
   using E = Elem<T>;
   constexpr int CHUNK_KEYS = chunk_keys<T, D>();
@@ -171,13 +177,15 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int j = 0; j < KPT; ++j) {
       const int t = threadIdx.x + j * NTH;
       const int row = t / KP_ROW, pc = t % KP_ROW;
-      rg.kr[j] = gld16((const uint8_t*)kbase + ((uint32_t)(c0 + row) * (D * ES) + pc * 16));
+      const uint8_t* src = (const uint8_t*)kbase + ((uint32_t)(c0 + row) * (D * ES) + pc * 16);
+      rg.kr[j] = NT ? gld16_nt(src) : gld16(src);
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int t = threadIdx.x + j * NTH;
       const int dr = t / VP_ROW, pc = t % VP_ROW;
-      rg.vr[j] = gld16((const uint8_t*)vbase + ((uint32_t)(dr * vstride + c0 + pc * EPP) * ES));
+      const uint8_t* src = (const uint8_t*)vbase + ((uint32_t)(dr * vstride + c0 + pc * EPP) * ES);
+      rg.vr[j] = NT ? gld16_nt(src) : gld16(src);
     }
   };
   auto lstore = [&](Regs& rg, int buf, int c0, int cend) {
@@ -782,6 +790,12 @@ static unsigned attn_grid(const AttnArgs& a, int qg_per_wg) {
   return (units + 7u) / 8u * 8u * (unsigned)((a.qgroups + qg_per_wg - 1) / qg_per_wg);
 }
 
+template <typename T, int D, int QG, int QT>
+static void launch_ak(bool nt, dim3 grid, hipStream_t s, const AttnArgs& a) {
+  if (nt) hipLaunchKernelGGL((attention_kernel<T, D, QG, QT, true>), grid, dim3(256 * QG), 0, s, a);
+  else hipLaunchKernelGGL((attention_kernel<T, D, QG, QT, false>), grid, dim3(256 * QG), 0, s, a);
+}
+
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a_in, hipStream_t s) {
   AttnArgs a = a_in;
@@ -794,13 +808,14 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t s) {
     nblk += (unsigned)a.warm.consumers;
   }
   dim3 grid(nblk);
+  const bool nt = a.stream != 0;
   switch (a.d * 8 + GPW) {
-    case 64 * 8 + 1: hipLaunchKernelGGL((attention_kernel<T, 64, 1, 1>), grid, dim3(256), 0, s, a); break;
-    case 64 * 8 + 2: hipLaunchKernelGGL((attention_kernel<T, 64, 2, 1>), grid, dim3(512), 0, s, a); break;
-    case 128 * 8 + 1: hipLaunchKernelGGL((attention_kernel<T, 128, 1, 1>), grid, dim3(256), 0, s, a); break;
-    case 128 * 8 + 2: hipLaunchKernelGGL((attention_kernel<T, 128, 2, 1>), grid, dim3(512), 0, s, a); break;
+    case 64 * 8 + 1: launch_ak<T, 64, 1, 1>(nt, grid, s, a); break;
+    case 64 * 8 + 2: launch_ak<T, 64, 2, 1>(nt, grid, s, a); break;
+    case 128 * 8 + 1: launch_ak<T, 128, 1, 1>(nt, grid, s, a); break;
+    case 128 * 8 + 2: launch_ak<T, 128, 2, 1>(nt, grid, s, a); break;
     case 64 * 8 + 4:
-      if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((attention_kernel<T, 64, 2, 2>), grid, dim3(512), 0, s, a);
+      if constexpr (sizeof(T) == 2) launch_ak<T, 64, 2, 2>(nt, grid, s, a);
       else return hipErrorInvalidValue;
       break;
     case 128 * 8 + 4:

@@ -181,6 +181,9 @@ struct AttnArgs {
   // block verification: every key comes from the cache (the block's were
   // stored there by the QKV product), block row i sees keys 0..ctx_len+i
   int32_t causal;
+  // the context K/V read per block is too large to stay cached between
+  // blocks: the register-staged kernel loads it nontemporally
+  int32_t stream;
 };
 // Splits of one (sequence, KV head): context keys, then block keys (or, in
 // the causal form, ctx_len + K cache keys).

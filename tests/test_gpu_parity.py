@@ -92,15 +92,18 @@ def test_padding_rows_never_leak():
     assert np.all(np.isfinite(g["logits"]))
 
 
+@pytest.mark.parametrize("stream", [False, True])
 @pytest.mark.parametrize("K", [16, 37, 130])
-def test_small_bf16_long_splits_poisoned(monkeypatch, K):
+def test_small_bf16_long_splits_poisoned(monkeypatch, K, stream):
     """Key splits of 1024 (16 chunks of 64: the staged attention pipelines'
     steady state and drain), ragged contexts whose last chunk is partial,
     NaN in every cache row past ctx_len; K = 16 (one query group), 37 (two
     query groups, one of them padding) and 130 (nine query groups: workgroups
-    of four, two query tiles per wave, the last workgroup mostly padding)."""
-    say(f"case: long splits K={K}")
+    of four, two query tiles per wave, the last workgroup mostly padding);
+    with `stream` the context K/V is loaded nontemporally."""
+    say(f"case: long splits K={K} stream={stream}")
     monkeypatch.setenv("DFLASH_ATTN_MIN_SPLIT", "1024")
+    monkeypatch.setenv("DFLASH_ATTN_STREAM_MB", "0" if stream else "1048576")
     p = Pair(SMALL, 41, 2, gain_std=0.1)
     _prefill(p, [1500, 2111])
     p.poison_padding()

@@ -112,13 +112,15 @@ def test_verify_bf16_batch2_ragged_contexts(K1):
         p.commit([K1 if step == 0 else rng.integers(0, K1 + 1), rng.integers(0, K1 + 1)])
 
 
+@pytest.mark.parametrize("stream", [False, True])
 @pytest.mark.parametrize("K1", [16, 40])
-def test_verify_bf16_d128_long_splits(monkeypatch, K1):
+def test_verify_bf16_d128_long_splits(monkeypatch, K1, stream):
     """head_dim 128 with bf16 weights (fp16 attention operands staged by
     direct loads to LDS), causal, with 1024-key splits: a 700-row prefill
     (11 chunks) and blocks over ragged contexts of several chunks each."""
-    say(f"verify bf16 d128 long splits K1={K1}")
+    say(f"verify bf16 d128 long splits K1={K1} stream={stream}")
     monkeypatch.setenv("DFLASH_ATTN_MIN_SPLIT", "1024")
+    monkeypatch.setenv("DFLASH_ATTN_STREAM_MB", "0" if stream else "1048576")
     shape = SMALL_T.replace(head_dim=128)
     p = VerifyPair(shape, (0, 2), 2, seed=26)
     rng = np.random.default_rng(6)
