@@ -18,19 +18,20 @@ constexpr int kCUs = 256;
 // tiles-per-workgroup variants compiled for each m-tile count, and the
 // largest one used: with many activation rows a workgroup re-reads every row
 // for its tiles, so wider tile ranges cut that traffic (accumulators of up to
-// 40 tiles live in the accumulation registers)
+// 32 tiles live in the accumulation registers; eight m-tiles with the hi/lo
+// pair fit four tiles per workgroup without spilling)
 static int round_ntg(int mtt, int want) {
   static const int v1[] = {1, 2, 4, 5, 6, 8};
   static const int v2[] = {1, 2, 4, 5, 8};
   static const int v4[] = {1, 2, 4, 5, 8};
-  static const int v8[] = {1, 2, 4, 5};
+  static const int v8[] = {1, 2, 4};
   const int* v = mtt == 1 ? v1 : mtt == 2 ? v2 : mtt == 4 ? v4 : v8;
-  const int n = mtt == 1 ? 6 : mtt == 8 ? 4 : 5;
+  const int n = mtt == 1 ? 6 : mtt == 8 ? 3 : 5;
   for (int i = 0; i < n; ++i)
     if (v[i] >= want) return v[i];
   return v[n - 1];
 }
-static int max_ntg(int mtt) { return mtt == 8 ? 5 : 8; }
+static int max_ntg(int mtt) { return mtt == 8 ? 4 : 8; }
 
 // The context-path products keep a fixed shape at prefill sizes (more than
 // two m-tiles: they run once); the per-step ones (the accepted rows, at
@@ -47,7 +48,13 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
   p.mtt = mtiles <= 1 ? 1 : mtiles <= 2 ? 2 : mtiles <= 4 ? 4 : 8;
   p.m_groups = (mtiles + p.mtt - 1) / p.mtt;
   p.rowmajor = rowmajor;
-  p.split = split_ok && !rowmajor && (p.mtt <= 2 || epi == EPI_KV);
+  // hi/lo pair for every product but the LM head above two m-tiles: the
+  // rounding of its input to bf16 reaches the logits alone, while that of
+  // a layer's inputs is carried through the later layers (measured by
+  // simulation at the Llama-3.1-8B shape, K = 128: max row error 1.03e-2
+  // with the pair everywhere, 1.06e-2 with the LM head's hi part alone,
+  // 3.4e-2 with the hi part everywhere)
+  p.split = split_ok && !rowmajor && (epi != EPI_ARGMAX || p.mtt <= 2);
   const int T = W.n_tiles;
   if (epi == EPI_PART) {
     int ns = 8;

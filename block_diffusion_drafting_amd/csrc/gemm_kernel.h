@@ -483,18 +483,16 @@ inline hipError_t launch_h(const GemmPlan& p, const GemmArgs& g, const EpiArgs& 
   return launch_v<T, MTT, NTG, EPI, ROW, SPLIT, WAVES, CHK, PIPE>(p, g, e, s);
 }
 
-// Compiled combinations: bf16 draft products use the hi/lo activation pair
-// when a workgroup holds at most two m-tiles; the per-step context
-// products (row-major features, K/V injection) have at most two m-tiles,
-// and K/V injection always uses the pair for bf16.
+// Compiled combinations: bf16 products take the hi/lo activation pair at
+// every m-tile count, the LM head up to two m-tiles (above that it runs
+// head_kernel on the hi part); the per-step context products (row-major
+// features, K/V injection) have at most two m-tiles.
 template <typename T, int MTT, int EPI, bool ROW, bool SPLIT>
 constexpr bool compiled() {
   if constexpr (ROW) return !SPLIT && MTT <= 2;
   if constexpr (EPI == EPI_KV) return MTT <= 2 && SPLIT == (sizeof(T) == 2);
-  // QKV of a fused step (block + context rows, up to four m-tiles) keeps
-  // the pair for the injected context K/V
-  if constexpr (EPI == EPI_QKV && sizeof(T) == 2 && MTT == 4) return true;
-  return sizeof(T) == 4 ? !SPLIT : (SPLIT == (MTT <= 2));
+  if constexpr (EPI == EPI_ARGMAX && sizeof(T) == 2) return SPLIT == (MTT <= 2);
+  return SPLIT == (sizeof(T) == 2);
 }
 
 template <typename T, int MTT, int EPI, bool ROW, bool SPLIT>
@@ -506,13 +504,13 @@ inline hipError_t launch_mtt(const GemmPlan& p, const GemmArgs& g, const EpiArgs
       case 1: return launch_h<T, MTT, 1, EPI, ROW, SPLIT>(p, g, e, s);
       case 2: return launch_h<T, MTT, 2, EPI, ROW, SPLIT>(p, g, e, s);
       case 4: return launch_h<T, MTT, 4, EPI, ROW, SPLIT>(p, g, e, s);
-      case 5: return launch_h<T, MTT, 5, EPI, ROW, SPLIT>(p, g, e, s);
+    }
+    if constexpr (MTT <= 4) {
+      if (p.ntg == 5) return launch_h<T, MTT, 5, EPI, ROW, SPLIT>(p, g, e, s);
+      if (p.ntg == 8) return launch_h<T, MTT, 8, EPI, ROW, SPLIT>(p, g, e, s);
     }
     if constexpr (MTT == 1) {
       if (p.ntg == 6) return launch_h<T, MTT, 6, EPI, ROW, SPLIT>(p, g, e, s);
-    }
-    if constexpr (MTT <= 4) {
-      if (p.ntg == 8) return launch_h<T, MTT, 8, EPI, ROW, SPLIT>(p, g, e, s);
     }
     return hipErrorInvalidValue;
   }
@@ -541,31 +539,32 @@ inline hipError_t launch_fixed(const GemmPlan& p, const GemmArgs& g, const EpiAr
 }
 
 // ---------------------------------------------------------------------------
-// LM head over m-groups of MTT = 8 or 4 m-tiles (128 or 64 rows; bf16
-// model, activations without the lo part): the waves of a workgroup split its tiles (up to NTW each, the whole
-// reduction each), so one copy of each activation fragment, staged in LDS,
-// feeds every wave; in the k-split form above, every workgroup of five
-// tiles re-reads the whole activation from L2 and each wave keeps one load
-// batch in flight.  Stages of KC k-blocks x MTT m-tiles are double
-// buffered; the next stage's activation and weight loads are in flight
+// Products over m-groups of MTT = 8 or 4 m-tiles (128 or 64 rows; bf16
+// model; the LM head on the hi part of the activations, and gate/up on the
+// hi/lo pair when there are enough m-groups): the waves of a workgroup
+// split its tiles (up to NTW each, the whole reduction each), so one copy
+// of each activation fragment, staged in LDS, feeds every wave; in the form
+// above, every workgroup of four or five tiles re-reads the whole
+// activation from L2 and each wave keeps one load batch in flight.  Stages
+// of KC k-blocks x MTT m-tiles are double buffered; the next stage's
+// activation and weight loads are in flight
 // while the current one is computed, and the last stage is peeled so that
 // every load in the loop is unconditional (a weight tile past the wave's
 // range re-reads its last tile, never used; activation k-blocks past the
-// end are zero).  The epilogue is the argmax epilogue of gemm_kernel, per
-// tile, on complete sums.
+// end are zero).  The epilogue is that of gemm_kernel, per tile, on
+// complete sums.
 // ---------------------------------------------------------------------------
-constexpr int HEAD_WAVES = 8;
-constexpr int HEAD_NTW = 3;   // tiles per wave at most
 constexpr int HEAD_KC = 2;    // k-blocks per stage
 
-template <typename T, int MTT>
+template <typename T, int MTT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void head_kernel(GemmArgs g,
                                                                                                   EpiArgs e) {
   using E = Elem<T>;
   constexpr int NTW = HEAD_NTW, KC = HEAD_KC, NTH = HEAD_WAVES * 64;
   constexpr int XPT = KC * MTT * WAVE / NTH;   // activation fragments staged per thread
+  constexpr int NX = SPLIT ? 2 : 1;            // hi (and lo) parts
   static_assert(XPT * NTH == KC * MTT * WAVE, "stage");
-  __shared__ u32x4 xs[2][KC][MTT][WAVE];
+  __shared__ u32x4 xs[NX][2][KC][MTT][WAVE];
   __shared__ unsigned long long kmax[MTT][16];
   __shared__ float rnorm[MTT * 16];
 
@@ -602,8 +601,8 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // norm scale of the 128 rows: thread (part p, row r) adds groups p, p + P, ...
-  {
+  // norm scale of the rows: thread (part p, row r) adds groups p, p + P, ...
+  if constexpr (needs_norm(EPI)) {
     constexpr int R = MTT * 16, P = NTH / R;
     __shared__ float npart[P][R];
     const int r = threadIdx.x % R, part = threadIdx.x / R;
@@ -612,7 +611,6 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     if (m < e.M)
       for (int q = part; q < e.ssq_groups; q += P) sum += e.ssq[(size_t)q * e.M + m];
     npart[part][r] = sum;
-    if (threadIdx.x < MTT * 16) (&kmax[0][0])[threadIdx.x] = 0ull;
     __syncthreads();
     if (threadIdx.x < R) {
       float tt = 0.f;
@@ -623,7 +621,7 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   }
 
   struct Stage {
-    u32x4 x[XPT];
+    u32x4 x[NX][XPT];
     u32x4 w[NTW][KC];
   };
   // stage s: k-blocks s*KC .. s*KC+KC-1 (past nkb: activation zero, weight
@@ -637,7 +635,11 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
       const bool ok = kb < nkb && mt0 + mt < g.X.mtiles;
       const size_t slot = ((size_t)min(mt0 + mt, g.X.mtiles - 1) * g.X.nkb + min(kb, nkb - 1)) * WAVE + ln;
       const u32x4 v = g.X.hi[slot];
-      st.x[j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      st.x[0][j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (SPLIT) {
+        const u32x4 vl = g.X.lo[slot];
+        st.x[1][j] = ok ? vl : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
@@ -651,24 +653,33 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int i = threadIdx.x + j * NTH;
-      (&xs[buf][0][0][0])[i] = st.x[j];
+#pragma unroll
+      for (int h = 0; h < NX; ++h) (&xs[h][buf][0][0][0])[i] = st.x[h][j];
     }
   };
   auto compute = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      u32x4 xf[MTT];
+      u32x4 xf[NX][MTT];
 #pragma unroll
-      for (int mt = 0; mt < MTT; ++mt) xf[mt] = xs[buf][k][mt][lane];
+      for (int h = 0; h < NX; ++h)
+#pragma unroll
+        for (int mt = 0; mt < MTT; ++mt) xf[h][mt] = xs[h][buf][k][mt][lane];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
         if (t >= wnt) continue;   // uniform over the wave
 #pragma unroll
-        for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = E::mma(st.w[t][k], xf[mt], acc[t][mt]);
+        for (int mt = 0; mt < MTT; ++mt) {
+          acc[t][mt] = E::mma(st.w[t][k], xf[0][mt], acc[t][mt]);
+          if constexpr (SPLIT) acc[t][mt] = E::mma(st.w[t][k], xf[1][mt], acc[t][mt]);
+        }
       }
     }
   };
 
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (threadIdx.x < MTT * 16) (&kmax[0][0])[threadIdx.x] = 0ull;   // visible after the first barrier
+  }
   const int nst = (nkb + KC - 1) / KC;
   Stage a, b;
   load(a, 0);
@@ -692,29 +703,22 @@ __global__ __launch_bounds__(HEAD_WAVES * 64) __attribute__((amdgpu_waves_per_eu
     if (t >= wnt) continue;
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt)
-      epilogue_tile<T, EPI_ARGMAX>(e, 0, wt0 + t, mt0 + mt, acc[t][mt], lane, rnorm[mt * 16 + (lane & 15)],
-                                   kmax[mt]);
+      epilogue_tile<T, EPI>(e, 0, wt0 + t, mt0 + mt, acc[t][mt], lane,
+                            needs_norm(EPI) ? rnorm[mt * 16 + (lane & 15)] : 1.f, kmax[mt]);
   }
-  __syncthreads();
-  if (threadIdx.x < MTT * 16) {
-    const int m = (mt0 + threadIdx.x / 16) * 16 + (threadIdx.x & 15);
-    const unsigned long long k = (&kmax[0][0])[threadIdx.x];
-    if (m < e.M && k) atomicMax(e.keys + m, k);
+  if constexpr (EPI == EPI_ARGMAX) {
+    __syncthreads();
+    if (threadIdx.x < MTT * 16) {
+      const int m = (mt0 + threadIdx.x / 16) * 16 + (threadIdx.x & 15);
+      const unsigned long long k = (&kmax[0][0])[threadIdx.x];
+      if (m < e.M && k) atomicMax(e.keys + m, k);
+    }
   }
 }
 
-// Tile groups of the head kernel: about two rounds of 256 workgroups, at
-// most HEAD_WAVES * HEAD_NTW tiles each.
-inline int head_groups(int n_tiles) {
-  const int cap = HEAD_WAVES * HEAD_NTW;
-  int G = n_tiles < 512 ? n_tiles : 512;
-  if ((n_tiles + G - 1) / G > cap) G = (n_tiles + cap - 1) / cap;
-  return G;
-}
-
-template <typename T>
+template <typename T, int EPI>
 inline hipError_t launch_head(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
-  g.n_groups = head_groups(g.W.n_tiles);
+  g.n_groups = head_groups(g.W.n_tiles, p.m_groups);
   g.m_groups = p.m_groups;
   g.nsplit = 1;
   g.kbu = g.W.nkb;
@@ -723,16 +727,18 @@ inline hipError_t launch_head(const GemmPlan& p, GemmArgs g, const EpiArgs& e, h
     return hipErrorInvalidValue;
   const unsigned units = (unsigned)g.n_groups;
   dim3 grid(p.m_groups > 1 ? (units + 7u) / 8u * 8u * (unsigned)p.m_groups : units);
-  if (p.mtt == 8) hipLaunchKernelGGL((head_kernel<T, 8>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
-  else if (p.mtt == 4) hipLaunchKernelGGL((head_kernel<T, 4>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
+  constexpr bool SPLIT = EPI != EPI_ARGMAX;   // the LM head reads the hi part alone
+  if (p.split != SPLIT || (SPLIT && !g.X.lo)) return hipErrorInvalidValue;
+  if (p.mtt == 8) hipLaunchKernelGGL((head_kernel<T, 8, EPI, SPLIT>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
+  else if (p.mtt == 4) hipLaunchKernelGGL((head_kernel<T, 4, EPI, SPLIT>), grid, dim3(HEAD_WAVES * 64), 0, s, g, e);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <typename T, int EPI>
 hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
-  if constexpr (EPI == EPI_ARGMAX && sizeof(T) == 2) {
-    if (uses_head_kernel(EPI, p, (int)sizeof(T))) return launch_head<T>(p, g, e, s);
+  if constexpr ((EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) && sizeof(T) == 2) {
+    if (uses_head_kernel(EPI, p, g.W.n_tiles, (int)sizeof(T))) return launch_head<T, EPI>(p, g, e, s);
   }
   g.kbu = p.kbu;
   g.nsplit = p.nsplit;

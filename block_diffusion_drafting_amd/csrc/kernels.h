@@ -112,12 +112,34 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor);
 
-// The LM head of a bf16 model over m-groups of 8 or 4 m-tiles (activations
-// without the lo part) runs head_kernel, whose waves split the tiles and
-// share the activations through LDS, instead of the k-split product kernel.
-inline bool uses_head_kernel(int epi, const GemmPlan& p, int elem_bytes) {
-  return epi == EPI_ARGMAX && elem_bytes == 2 && (p.mtt == 8 || p.mtt == 4) && !p.split && !p.rowmajor &&
-         !p.fixed;
+// head_kernel: HEAD_WAVES waves per workgroup, each over up to HEAD_NTW
+// weight tiles with the whole reduction, sharing the activations via LDS.
+constexpr int HEAD_WAVES = 8;
+constexpr int HEAD_NTW = 3;
+
+// Tile groups per m-group of head_kernel: about two rounds of 256
+// workgroups over all m-groups, at most HEAD_WAVES * HEAD_NTW tiles each.
+inline int head_groups(int n_tiles, int m_groups) {
+  const int cap = HEAD_WAVES * HEAD_NTW;
+  const int want = (512 + m_groups - 1) / m_groups;
+  int G = n_tiles < want ? n_tiles : want;
+  if ((n_tiles + G - 1) / G > cap) G = (n_tiles + cap - 1) / cap;
+  return G;
+}
+
+// Products of a bf16 model that run head_kernel instead of gemm_kernel:
+// the LM head over m-groups of 8 or 4 m-tiles (hi part of the
+// activations), and gate/up over m-groups of 8 m-tiles (hi/lo pair) when
+// there are enough of them to give each wave two tiles or more.  With fewer tiles per wave its
+// waves keep too few loads in flight (measured on MI355X: at two m-groups
+// of the Qwen3-4B gate/up it takes 1.8x the time of gemm_kernel, at eight
+// m-groups 0.68x).
+inline bool uses_head_kernel(int epi, const GemmPlan& p, int n_tiles, int elem_bytes) {
+  if (elem_bytes != 2 || p.rowmajor || p.fixed) return false;
+  if (epi == EPI_ARGMAX) return !p.split && (p.mtt == 8 || p.mtt == 4);
+  if (epi != EPI_SWIGLU || !p.split || p.mtt != 8) return false;
+  const int G = head_groups(n_tiles, p.m_groups);
+  return (n_tiles + G - 1) / G >= 2 * HEAD_WAVES;
 }
 
 template <typename T>

@@ -392,6 +392,20 @@ def test_workload2_llama_shape_growth_session():
 
 
 @pytest.mark.slow
+def test_llama_shape_large_block():
+    """Llama-3.1-8B-shaped drafter, one block of K=640 (five groups of 128
+    rows) over a 1500-row context: with that many row groups the gate/up
+    product runs on the shared-activation kernel (two tiles or more per
+    wave), and so does the LM head."""
+    say("case: llama shape, ctx 1500, K 640")
+    wl = synth.workload(2)
+    p = Pair(wl.shape, wl.seed, 1, weights=_weights(wl.shape, wl.seed))
+    _prefill(p, [1500], seed=wl.seed)
+    ids = _ids(wl.seed + 1, 1, 640, wl.shape.vocab)
+    p.compare(ids, hidden=False)
+
+
+@pytest.mark.slow
 def test_workload4_batched_long_context_sampled():
     """Batch 16, contexts 1k-32k: the GPU runs all 16 sequences; the oracle
     follows two sampled sequences (the shortest and one mid-length) for the
