@@ -505,8 +505,10 @@ inline hipError_t launch_mtt(const GemmPlan& p, const GemmArgs& g, const EpiArgs
       case 2: return launch_h<T, MTT, 2, EPI, ROW, SPLIT>(p, g, e, s);
       case 4: return launch_h<T, MTT, 4, EPI, ROW, SPLIT>(p, g, e, s);
     }
-    if constexpr (MTT <= 4) {
+    if constexpr (MTT <= 4 || EPI == EPI_PART) {
       if (p.ntg == 5) return launch_h<T, MTT, 5, EPI, ROW, SPLIT>(p, g, e, s);
+    }
+    if constexpr (MTT <= 4) {
       if (p.ntg == 8) return launch_h<T, MTT, 8, EPI, ROW, SPLIT>(p, g, e, s);
     }
     if constexpr (MTT == 1) {
