@@ -60,16 +60,19 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
   // with the pair everywhere, 1.06e-2 with the LM head's hi part alone,
   // 3.4e-2 with the hi part everywhere)
   p.split = split_ok && !rowmajor && (epi != EPI_ARGMAX || p.mtt <= 2);
-  // 64-row m-groups for QKV and gate/up with the hi/lo pair: every
-  // workgroup re-reads the whole activation of its m-group from L2, so two
-  // groups of 64 rows halve that per workgroup, the weights of a tile range
-  // being read once from HBM for both (XCD-grouped numbering of gemm_kernel).
-  // Measured at the Qwen3-4B shape: QKV + gate/up per K = 128 block 499 ->
-  // 385 us, gate/up at batch 16 600 -> 523 us.  QKV keeps 128-row groups
-  // above 128 rows (slower at batch 16), gate/up where the head kernel
-  // takes it.
-  if (p.split && p.mtt == 8 &&
-      (epi == EPI_QKV ? mtiles <= 8 : epi == EPI_SWIGLU && !uses_head_kernel(epi, p, W.n_tiles, 2))) {
+  // Smaller m-groups for QKV and gate/up with the hi/lo pair: every
+  // workgroup re-reads the whole activation of its m-group from L2, so
+  // groups of 32 or 64 rows cut that per workgroup, the weights of a tile
+  // range being read once from HBM for all of them (XCD-grouped numbering
+  // of gemm_kernel).  Measured at the Qwen3-4B shape: QKV in 32-row groups
+  // up to 128 rows (per K = 128 block 185 -> 118 us, K = 64 116 -> 93 us;
+  // slower at batch 16, 256 rows), gate/up in 64-row groups unless the head
+  // kernel takes it (K = 128 314 -> 240 us, batch 16 600 -> 517 us; 32-row
+  // groups slower).
+  if (p.split && epi == EPI_QKV && mtiles > 2 && mtiles <= 8) {
+    p.mtt = 2;
+    p.m_groups = (mtiles + 1) / 2;
+  } else if (p.split && p.mtt == 8 && epi == EPI_SWIGLU && !uses_head_kernel(epi, p, W.n_tiles, 2)) {
     p.mtt = 4;
     p.m_groups = (mtiles + 3) / 4;
   }
