@@ -68,8 +68,9 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
   // up to 128 rows (per K = 128 block 185 -> 118 us, K = 64 116 -> 93 us;
   // slower at batch 16, 256 rows), gate/up in 64-row groups unless the head
   // kernel takes it (K = 128 314 -> 240 us, batch 16 600 -> 517 us; 32-row
-  // groups slower).
-  if (p.split && epi == EPI_QKV && mtiles > 2 && mtiles <= 8) {
+  // groups slower); the k-split products (o, down) in 32-row groups up to
+  // 64 rows (K = 64 214 -> 175 us; slower in 64-row groups at 128 rows).
+  if (p.split && ((epi == EPI_QKV && mtiles <= 8) || (epi == EPI_PART && mtiles <= 4)) && mtiles > 2) {
     p.mtt = 2;
     p.m_groups = (mtiles + 1) / 2;
   } else if (p.split && p.mtt == 8 && epi == EPI_SWIGLU && !uses_head_kernel(epi, p, W.n_tiles, 2)) {
