@@ -392,17 +392,21 @@ def test_workload2_llama_shape_growth_session():
 
 
 @pytest.mark.slow
-def test_llama_shape_large_block():
-    """Llama-3.1-8B-shaped drafter, one block of K=640 (five groups of 128
-    rows) over a 1500-row context: with that many row groups the gate/up
-    product runs on the shared-activation kernel (two tiles or more per
-    wave), and so does the LM head."""
-    say("case: llama shape, ctx 1500, K 640")
+@pytest.mark.parametrize("K", [48, 128, 640])
+def test_llama_shape_large_block(K):
+    """Llama-3.1-8B-shaped drafter, one block over a 1500-row context, above
+    the 32 rows where the products' activation precision used to drop:
+    K=48 (three 16-row tiles: QKV and the k-split products in 32-row
+    groups, gate/up in one 64-row group, the LM head on 64 rows), K=128
+    (gate/up in two 64-row groups, the k-split products over 128 rows) and
+    K=640 (five 128-row groups: gate/up and the LM head on the
+    shared-activation kernel)."""
+    say(f"case: llama shape, ctx 1500, K {K}")
     wl = synth.workload(2)
     p = Pair(wl.shape, wl.seed, 1, weights=_weights(wl.shape, wl.seed))
     _prefill(p, [1500], seed=wl.seed)
-    ids = _ids(wl.seed + 1, 1, 640, wl.shape.vocab)
-    p.compare(ids, hidden=False)
+    ids = _ids(wl.seed + 1, 1, K, wl.shape.vocab)
+    p.compare(ids, hidden=(K <= 128))
 
 
 @pytest.mark.slow
