@@ -23,15 +23,17 @@ constexpr int kCUs = 256;
 // products (EPI_PART) take five, spilling a few registers, because the
 // fewer workgroups re-read less of the activations (measured on the
 // Qwen3-4B shape: o + down at K = 128 262 -> 226 us per block, batch 16
-// 480 -> 381 us; gate/up and QKV slower with five)
-static int max_ntg(int mtt, int epi) { return mtt == 8 ? (epi == EPI_PART ? 5 : 4) : 8; }
+// 480 -> 381 us; gate/up and QKV slower with five).  Four m-tiles take at
+// most five: with eight a workgroup runs at one wave per SIMD (gate/up in
+// 64-row groups at batch 16 516 -> 390 us per block with five).
+static int max_ntg(int mtt, int epi) { return mtt == 8 ? (epi == EPI_PART ? 5 : 4) : mtt == 4 ? 5 : 8; }
 static int round_ntg(int mtt, int epi, int want) {
   static const int v1[] = {1, 2, 4, 5, 6, 8};
   static const int v2[] = {1, 2, 4, 5, 8};
-  static const int v4[] = {1, 2, 4, 5, 8};
+  static const int v4[] = {1, 2, 4, 5};
   static const int v8[] = {1, 2, 4, 5};
   const int* v = mtt == 1 ? v1 : mtt == 2 ? v2 : mtt == 4 ? v4 : v8;
-  const int n = mtt == 1 ? 6 : mtt == 8 ? 4 : 5;
+  const int n = mtt == 1 ? 6 : mtt == 2 ? 5 : 4;
   const int cap = max_ntg(mtt, epi);
   for (int i = 0; i < n && v[i] <= cap; ++i)
     if (v[i] >= want) return v[i];
