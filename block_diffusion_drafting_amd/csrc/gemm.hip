@@ -25,16 +25,22 @@ constexpr int kCUs = 256;
 // Qwen3-4B shape: o + down at K = 128 262 -> 226 us per block, batch 16
 // 480 -> 381 us; gate/up and QKV slower with five).  Four m-tiles take at
 // most five: with eight a workgroup runs at one wave per SIMD (gate/up in
-// 64-row groups at batch 16 516 -> 390 us per block with five).
-static int max_ntg(int mtt, int epi) { return mtt == 8 ? (epi == EPI_PART ? 5 : 4) : mtt == 4 ? 5 : 8; }
-static int round_ntg(int mtt, int epi, int want) {
+// 64-row groups at batch 16 516 -> 390 us per block with five); QKV over
+// sixteen m-groups or more still gains more from the fewer re-reads (K =
+// 1024 630 -> 500 us per block with eight; at eight m-groups, 512 rows,
+// eight was slower).
+static int max_ntg(int mtt, int epi, int m_groups) {
+  if (mtt == 8) return epi == EPI_PART ? 5 : 4;
+  if (mtt == 4) return epi == EPI_QKV && m_groups >= 16 ? 8 : 5;
+  return 8;
+}
+static int round_ntg(int mtt, int cap, int want) {
   static const int v1[] = {1, 2, 4, 5, 6, 8};
   static const int v2[] = {1, 2, 4, 5, 8};
-  static const int v4[] = {1, 2, 4, 5};
+  static const int v4[] = {1, 2, 4, 5, 8};
   static const int v8[] = {1, 2, 4, 5};
   const int* v = mtt == 1 ? v1 : mtt == 2 ? v2 : mtt == 4 ? v4 : v8;
-  const int n = mtt == 1 ? 6 : mtt == 2 ? 5 : 4;
-  const int cap = max_ntg(mtt, epi);
+  const int n = mtt == 1 ? 6 : mtt == 8 ? 4 : 5;
   for (int i = 0; i < n && v[i] <= cap; ++i)
     if (v[i] >= want) return v[i];
   return cap;
@@ -68,14 +74,17 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
   // range being read once from HBM for all of them (XCD-grouped numbering
   // of gemm_kernel).  Measured at the Qwen3-4B shape: QKV in 32-row groups
   // up to 128 rows (per K = 128 block 185 -> 118 us, K = 64 116 -> 93 us;
-  // slower at batch 16, 256 rows), gate/up in 64-row groups unless the head
+  // slower at batch 16, 256 rows) and in 64-row groups above 256 rows
+  // (K = 1024 699 -> 500 us), gate/up in 64-row groups unless the head
   // kernel takes it (K = 128 314 -> 240 us, batch 16 600 -> 517 us; 32-row
   // groups slower); the k-split products (o, down) in 32-row groups up to
   // 64 rows (K = 64 214 -> 175 us; slower in 64-row groups at 128 rows).
   if (p.split && ((epi == EPI_QKV && mtiles <= 8) || (epi == EPI_PART && mtiles <= 4)) && mtiles > 2) {
     p.mtt = 2;
     p.m_groups = (mtiles + 1) / 2;
-  } else if (p.split && p.mtt == 8 && epi == EPI_SWIGLU && !uses_head_kernel(epi, p, W.n_tiles, 2)) {
+  } else if (p.split && p.mtt == 8 &&
+             ((epi == EPI_QKV && mtiles > 16) ||
+              (epi == EPI_SWIGLU && !uses_head_kernel(epi, p, W.n_tiles, 2)))) {
     p.mtt = 4;
     p.m_groups = (mtiles + 3) / 4;
   }
@@ -98,10 +107,10 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
     return p;
   }
   const int per_round = kCUs / (p.nsplit * p.m_groups) > 0 ? kCUs / (p.nsplit * p.m_groups) : 1;
-  const int cap = max_ntg(p.mtt, epi);
+  const int cap = max_ntg(p.mtt, epi, p.m_groups);
   int groups = per_round * ((T + per_round * cap - 1) / (per_round * cap));
   if (groups > T) groups = T;
-  p.ntg = round_ntg(p.mtt, epi, (T + groups - 1) / groups);
+  p.ntg = round_ntg(p.mtt, cap, (T + groups - 1) / groups);
   p.n_groups = groups;
   return p;
 }

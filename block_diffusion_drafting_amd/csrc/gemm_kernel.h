@@ -508,7 +508,7 @@ inline hipError_t launch_mtt(const GemmPlan& p, const GemmArgs& g, const EpiArgs
     if constexpr (MTT <= 4 || EPI == EPI_PART) {
       if (p.ntg == 5) return launch_h<T, MTT, 5, EPI, ROW, SPLIT>(p, g, e, s);
     }
-    if constexpr (MTT <= 2) {
+    if constexpr (MTT <= 2 || (MTT == 4 && EPI == EPI_QKV)) {
       if (p.ntg == 8) return launch_h<T, MTT, 8, EPI, ROW, SPLIT>(p, g, e, s);
     }
     if constexpr (MTT == 1) {
