@@ -196,7 +196,11 @@ dflash_status dflash_project_ctx(dflash_ctx *c, const void *feats, const int32_t
  * and the whole block (no causal mask), output projection + residual,
  * RMSNorm, SwiGLU MLP + residual; then final RMSNorm, LM head, argmax
  * (kongchang.com, "System architecture", "Innovation 1"; Google Developers
- * Blog, "Dual cache for attention").  Does not change the state. */
+ * Blog, "Dual cache for attention").  Does not change the state.
+ * Arithmetic of DFLASH_BF16 models: bf16 weights, the residual stream in
+ * fp32, every product's activations fed as a bf16 hi/lo pair (about fp32)
+ * but the LM head's above 32 rows (bf16), fp32 sums; attention operands
+ * fp16, softmax in fp32. */
 dflash_status dflash_draft_block(dflash_ctx *c, const int32_t *block_ids, int32_t K,
                                  int32_t *draft_ids, float *logits, void *hidden,
                                  void *stream);
