@@ -139,6 +139,7 @@ class SeqState:
     k: Optional[List[np.ndarray]] = None     # per layer [ctx_len, nkv, d], RoPE applied
     v: Optional[List[np.ndarray]] = None     # per layer [ctx_len, nkv, d]
     grow_events: int = 0
+    store: dict = dataclasses.field(default_factory=dict, repr=False)   # backing arrays
 
 
 def new_state(model: Model) -> SeqState:
@@ -147,6 +148,27 @@ def new_state(model: Model) -> SeqState:
                     ctx=np.zeros((0, s.hidden)),
                     k=[np.zeros((0, s.n_kv_heads, s.head_dim)) for _ in range(s.n_layers)],
                     v=[np.zeros((0, s.n_kv_heads, s.head_dim)) for _ in range(s.n_layers)])
+
+
+def _append_rows(state: SeqState, key, cur: np.ndarray, new: np.ndarray) -> np.ndarray:
+    """``cur`` with the rows ``new`` appended, as a view of the first rows of
+    a backing array kept in ``state`` that grows by a quarter when full, so
+    that a long session of small appends copies each row a bounded number
+    of times (storage only: the values are those of a concatenation).  An
+    array that is not the view handed out last (a test replaced it) starts a
+    new backing array."""
+    n0, n1 = cur.shape[0], cur.shape[0] + new.shape[0]
+    back = state.store.get(key)
+    if (back is None or cur.base is not back or cur.shape[1:] != back.shape[1:]
+            or cur.__array_interface__["data"][0] != back.__array_interface__["data"][0]
+            or n1 > back.shape[0]):
+        cap = n1 + max(64, n1 // 4)
+        nb = np.empty((cap,) + tuple(cur.shape[1:]), dtype=np.result_type(cur, new))
+        nb[:n0] = cur
+        back = nb
+        state.store[key] = back
+    back[n0:n1] = new
+    return back[:n1]
 
 
 def grow_rule(ctx_len: int, cap: int, n_new: int) -> int:
@@ -188,10 +210,10 @@ def project_ctx(model: Model, state: SeqState, feats: np.ndarray,
         p = f"layers.{l}."
         kk = (c @ model.f64(p + "wk").T).reshape(n_new, s.n_kv_heads, s.head_dim)
         vv = (c @ model.f64(p + "wv").T).reshape(n_new, s.n_kv_heads, s.head_dim)
-        state.k[l] = np.concatenate([state.k[l], rope(kk, pos, s.rope_theta)], axis=0)
-        state.v[l] = np.concatenate([state.v[l], vv], axis=0)
-    state.ctx = np.concatenate([state.ctx, c], axis=0)
-    state.pos = np.concatenate([state.pos, pos])
+        state.k[l] = _append_rows(state, ("k", l), state.k[l], rope(kk, pos, s.rope_theta))
+        state.v[l] = _append_rows(state, ("v", l), state.v[l], vv)
+    state.ctx = _append_rows(state, "ctx", state.ctx, c)
+    state.pos = _append_rows(state, "pos", state.pos, pos)
     new_cap = grow_rule(state.ctx_len, state.cap, n_new)
     if new_cap != state.cap:
         state.grow_events += 1
