@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix peak
 METRIC = "draft-block latency (ms) & drafted tok/s at K=16, Qwen3-4B shape; % HBM peak"
 
 
@@ -55,6 +56,10 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=25)
     ap.add_argument("--ksweep", action="store_true")
     ap.add_argument("--draft-iters", type=int, default=50)
+    ap.add_argument("--dist-iters", type=int, default=200,
+                    help="timed draft blocks per warm / cold latency distribution")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cold-cache, K-flat, MFMA and Llama-shaped figures")
     ap.add_argument("--persistent", action="store_true",
                     help="draft with the single-launch block where it applies (batch * K <= 16)")
     ap.add_argument("--trace", action="store_true",
@@ -241,10 +246,159 @@ def cpu_baseline(wl, K, w, n_steps):
     for _ in range(n_steps):
         sess.step()
     dt = (time.time() - t0) / n_steps
+    cpu_model, host_cores = host_cpu()
     return {"value": round(wl.batch * K / dt, 3), "unit": "drafted tok/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "host_cores_available": host_cores,
             "sample": f"{n_steps} whole steps (fp64 draft block + accept + projection) of workload "
-                      f"'{wl.name}' after an untimed prefill and one untimed step; {dt:.2f} s/step"}
+                      f"'{wl.name}' after an untimed prefill and one untimed step; {dt:.2f} s/step; "
+                      f"'cores' is the BLAS thread count the oracle ran with"}
+
+
+def host_cpu():
+    """(CPU model name, cores this process may run on)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
+def block_flops(shape, ctx_lens, K, batch):
+    """Algorithmic flops of one draft block: every weight product once
+    (2 flops per multiply-add; the hi/lo activation pair the kernels issue
+    for precision is not counted) plus attention (Q K^T and P V over each
+    sequence's context and block keys)."""
+    s = shape
+    M = batch * K
+    params = s.n_layers * s.hidden * ((s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim + s.q_dim
+                                      + 3 * s.intermediate) + s.vocab * s.hidden
+    attn = sum(4 * K * s.n_q_heads * s.head_dim * (c + K) * s.n_layers for c in ctx_lens)
+    return 2 * M * params, attn
+
+
+def event_times(torch, stream, fn, iters, flush=None):
+    """Per-call milliseconds of fn() from HIP events recorded on `stream`
+    around each call; with `flush` (a 1 GiB device buffer) every call is
+    preceded, outside its events, by a write of the whole buffer, which
+    evicts the L2 caches and the 256 MB Infinity Cache."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(float(i & 7))
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def spread(ms):
+    return {"median": round(float(np.median(ms)), 4), "p10": round(float(np.percentile(ms, 10)), 4),
+            "p90": round(float(np.percentile(ms, 90)), 4), "mean": round(float(ms.mean()), 4), "n": int(ms.size)}
+
+
+def north_star_extras(args, torch, dfl, wl, model, ctx, K, ids0, lens0, mb):
+    """The figures the goal names beside the headline step: draft-block
+    latency warm and cold (median / p10 / p90), MFMA utilisation, the
+    draft latency at K = 16 and K = 128 over a 4096-position context (the
+    K sweep's context, same drafter shape), and the Llama-3.1-8B-shaped
+    drafter's block at K = 10 over 4096 positions."""
+    import synth
+    stream = torch.cuda.current_stream()
+    s = wl.shape
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    it = args.dist_iters
+    out = {}
+    draft = torch.empty(wl.batch, K, dtype=torch.int32, device="cuda")
+
+    def block():
+        dfl.dflash_draft_block(ctx, ids0, K, draft)
+
+    lens0, _ = ctx.query()           # the context as the timed steps left it
+    warm = event_times(torch, stream, block, it)
+    cold = event_times(torch, stream, block, it, flush)
+    byt = block_bytes(s, mb, lens0, K, wl.batch)
+    out["draft_block_warm_ms"] = spread(warm)
+    out["draft_block_cold_ms"] = spread(cold)
+    out["draft_block_cold_hbm_frac"] = round(byt / (np.median(cold) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    fp, fa = block_flops(s, lens0, K, wl.batch)
+    med = float(np.median(warm))
+    out["mfma"] = {"flops_per_block": int(fp + fa), "product_flops": int(fp), "attention_flops": int(fa),
+                   "achieved_tflops": round((fp + fa) / (med * 1e-3) / 1e12, 2),
+                   "peak_tflops": MFMA_PEAK_TFLOPS, "frac": round((fp + fa) / (med * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 5),
+                   "timing": "warm median draft block", "dtype": "bf16 products (hi/lo activation pair), "
+                                                            "fp16 attention"}
+    log(f"[bench] draft block warm median {med:.4f} ms, cold median {np.median(cold):.4f} ms")
+
+    # K-flat: the K sweep's 4096-position context on the same drafter shape
+    w3 = synth.workload(3)
+    c3 = dfl.Context(model, 1)
+    f3 = synth.prefill_features(w3.shape, w3.seed, 0, w3.ctx0[0])
+    dfl.dflash_project_ctx(c3, torch.from_numpy(f3).cuda(), [w3.ctx0[0]])
+    del f3
+    kf = {"ctx": w3.ctx0[0]}
+    for Kx in (16, 128):
+        ids = torch.from_numpy(synth.block_ids(w3.seed, 0, 0, Kx, s.vocab)).cuda().view(1, Kx)
+        dr = torch.empty(1, Kx, dtype=torch.int32, device="cuda")
+
+        def fn(ids=ids, dr=dr, Kx=Kx):
+            dfl.dflash_draft_block(c3, ids, Kx, dr)
+
+        for _ in range(3):
+            fn()
+        wm = event_times(torch, stream, fn, it)
+        cm = event_times(torch, stream, fn, it, flush)
+        kf[f"K{Kx}_warm_ms"] = spread(wm)
+        kf[f"K{Kx}_cold_ms"] = spread(cm)
+    kf["ratio_K128_over_K16_warm"] = round(kf["K128_warm_ms"]["median"] / kf["K16_warm_ms"]["median"], 4)
+    kf["ratio_K128_over_K16_cold"] = round(kf["K128_cold_ms"]["median"] / kf["K16_cold_ms"]["median"], 4)
+    kf["target"] = "<= 1.2"
+    out["k_flat"] = kf
+    c3.close()
+    log(f"[bench] K-flat at ctx 4096: {kf['ratio_K128_over_K16_warm']} warm, {kf['ratio_K128_over_K16_cold']} cold")
+
+    # Llama-3.1-8B-shaped drafter, K = 10, 4096 positions
+    w2 = synth.workload(2)
+    t0 = time.time()
+    wts = synth.weights(w2.shape, w2.seed)
+    m2 = dfl.Model(w2.shape, dfl.weights_to_device(wts))
+    del wts
+    c2 = dfl.Context(m2, 1)
+    f2 = synth.prefill_features(w2.shape, w2.seed, 0, w2.ctx0[0])
+    dfl.dflash_project_ctx(c2, torch.from_numpy(f2).cuda(), [w2.ctx0[0]])
+    del f2
+    log(f"[bench] llama-shaped drafter set up in {time.time() - t0:.1f}s")
+    ids = torch.from_numpy(synth.block_ids(w2.seed, 0, 0, w2.K, w2.shape.vocab)).cuda().view(1, w2.K)
+    dr = torch.empty(1, w2.K, dtype=torch.int32, device="cuda")
+
+    def fl():
+        dfl.dflash_draft_block(c2, ids, w2.K, dr)
+
+    for _ in range(3):
+        fl()
+    wm = event_times(torch, stream, fl, it)
+    cm = event_times(torch, stream, fl, it, flush)
+    b2 = block_bytes(w2.shape, m2.bytes(), [w2.ctx0[0]], w2.K, 1)
+    out[w2.name] = {"K": w2.K, "ctx": w2.ctx0[0], "bytes_per_block": int(b2),
+                    "draft_block_warm_ms": spread(wm), "draft_block_cold_ms": spread(cm),
+                    "drafted_tok_s_warm": round(w2.K / (np.median(wm) * 1e-3), 1),
+                    "hbm_frac_warm": round(b2 / (np.median(wm) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "hbm_frac_cold": round(b2 / (np.median(cm) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    c2.close()
+    m2.close()
+    del flush
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def decay_ce_cpu_baseline(L, t, n_rows):
@@ -806,6 +960,8 @@ def main():
                          "traffic": measured_traffic(dom, wl.name, K), "avg_launch_ms": round(dom_avg, 5),
                          "launches": dom_n, "bytes_per_launch": int(dom_bytes)},
         }
+        if not args.no_extras and args.workload == 1 and not args.K:
+            out.update(north_star_extras(args, torch, dfl, wl, model, ctx, K, dev[0][0], lens0, mb))
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(wl, K, w, args.cpu_steps)
         results.append(out)
@@ -820,6 +976,10 @@ def main():
                           "latency_ratio_K128_over_K16": round(flat, 4) if flat else None}))
     else:
         print(json.dumps(results[0]))
+    # release the library's device memory while torch is fully alive
+    torch.cuda.synchronize()
+    ctx.close()
+    model.close()
 
 
 if __name__ == "__main__":

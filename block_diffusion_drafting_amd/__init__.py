@@ -19,8 +19,12 @@ Entry points keep the C names:
 """
 from __future__ import annotations
 
+import atexit
+import contextlib
 import ctypes
 import os
+import sys
+import weakref
 from typing import Dict, Optional, Sequence
 
 import torch
@@ -158,6 +162,41 @@ def _stream(stream: Optional[torch.cuda.Stream]) -> int:
     return s.cuda_stream
 
 
+def _on(stream: Optional[torch.cuda.Stream]):
+    """Makes the call's stream torch's current stream while the library may
+    allocate or free (growth, workspaces): TorchAllocator then serves and
+    releases blocks on that stream, so torch reuses them only after the work
+    queued there."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+# Live handles, closed before interpreter shutdown: destroying a context or a
+# model frees device memory through Python callbacks into torch's allocator,
+# which must still be alive then.
+_LIVE: "weakref.WeakSet" = weakref.WeakSet()
+
+
+def _close_all() -> None:
+    objs = list(_LIVE)
+    if not objs:
+        return
+    try:
+        if torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+    except Exception:
+        pass
+    for kind in (Context, Model, AdaptPolicy):
+        for o in objs:
+            if isinstance(o, kind):
+                try:
+                    o.close()
+                except Exception:
+                    pass
+
+
+atexit.register(_close_all)
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
@@ -188,7 +227,15 @@ class TorchAllocator:
         return p
 
     def _free(self, p: int, user) -> None:
-        self.live.pop(int(p) if p else 0, None)
+        t = self.live.pop(int(p) if p else 0, None)
+        if t is not None and not sys.is_finalizing():
+            # work queued on the freeing call's stream (torch's current stream
+            # during the call) may still use the block: torch reuses it only
+            # after that work, also when it was allocated on another stream
+            try:
+                t.record_stream(torch.cuda.current_stream(self.device))
+            except Exception:
+                pass
 
     @property
     def bytes(self) -> int:
@@ -236,16 +283,19 @@ class Model:
             if len(self.taps) != shape.n_feat:
                 raise ValueError("a target's shape.n_feat must equal len(taps)")
             tp = (ctypes.c_int32 * max(len(self.taps), 1))(*[int(t) for t in self.taps])
-            _check("dflash_target_create",
-                   lib.dflash_target_create(ctypes.byref(cfg), ctypes.byref(w), tp,
-                                            ctypes.byref(self.alloc.struct), _stream(stream),
-                                            ctypes.byref(h)))
+            with _on(stream):
+                _check("dflash_target_create",
+                       lib.dflash_target_create(ctypes.byref(cfg), ctypes.byref(w), tp,
+                                                ctypes.byref(self.alloc.struct), _stream(stream),
+                                                ctypes.byref(h)))
         else:
-            _check("dflash_model_create",
-                   lib.dflash_model_create(ctypes.byref(cfg), ctypes.byref(w),
-                                           ctypes.byref(self.alloc.struct), _stream(stream),
-                                           ctypes.byref(h)))
+            with _on(stream):
+                _check("dflash_model_create",
+                       lib.dflash_model_create(ctypes.byref(cfg), ctypes.byref(w),
+                                               ctypes.byref(self.alloc.struct), _stream(stream),
+                                               ctypes.byref(h)))
         self.handle = h
+        _LIVE.add(self)
 
     def bytes(self):
         a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
@@ -259,6 +309,8 @@ class Model:
             self.handle = None
 
     def __del__(self):
+        if sys.is_finalizing():      # closed by the atexit hook, or torch is gone
+            return
         try:
             self.close()
         except Exception:
@@ -277,10 +329,12 @@ class Context:
         if init_cap is not None:
             caps = (ctypes.c_int32 * batch)(*[int(c) for c in init_cap])
         h = ctypes.c_void_p()
-        _check("dflash_ctx_create",
-               lib.dflash_ctx_create(model.handle, batch, caps, ctypes.byref(self.alloc.struct),
-                                     _stream(stream), ctypes.byref(h)))
+        with _on(stream):
+            _check("dflash_ctx_create",
+                   lib.dflash_ctx_create(model.handle, batch, caps, ctypes.byref(self.alloc.struct),
+                                         _stream(stream), ctypes.byref(h)))
         self.handle = h
+        _LIVE.add(self)
 
     def query(self):
         a = (ctypes.c_int32 * self.batch)()
@@ -358,6 +412,8 @@ class Context:
             self.handle = None
 
     def __del__(self):
+        if sys.is_finalizing():      # closed by the atexit hook, or torch is gone
+            return
         try:
             self.close()
         except Exception:
@@ -370,9 +426,10 @@ def dflash_project_ctx(ctx: Context, feats: torch.Tensor, n_new: Sequence[int],
     nn = (ctypes.c_int32 * ctx.batch)(*[int(n) for n in n_new])
     if positions is not None and positions.dtype != torch.int32:
         raise ValueError("positions must be int32")
-    _check("dflash_project_ctx",
-           lib.dflash_project_ctx(ctx.handle, _ptr(feats) if feats is not None and feats.numel() else None,
-                                  nn, _ptr(positions), _stream(stream)))
+    with _on(stream):
+        _check("dflash_project_ctx",
+               lib.dflash_project_ctx(ctx.handle, _ptr(feats) if feats is not None and feats.numel() else None,
+                                      nn, _ptr(positions), _stream(stream)))
 
 
 def dflash_draft_block(ctx: Context, block_ids: torch.Tensor, K: int, draft_ids: torch.Tensor,
@@ -384,9 +441,10 @@ def dflash_draft_block(ctx: Context, block_ids: torch.Tensor, K: int, draft_ids:
     if logits is not None and (logits.dtype != torch.float32 or
                                logits.numel() != ctx.batch * K * ctx.model.shape.vocab):
         raise ValueError("logits must be float32 [batch, K, vocab]")
-    _check("dflash_draft_block",
-           lib.dflash_draft_block(ctx.handle, _ptr(block_ids), int(K), _ptr(draft_ids),
-                                  _ptr(logits), _ptr(hidden), _stream(stream)))
+    with _on(stream):
+        _check("dflash_draft_block",
+               lib.dflash_draft_block(ctx.handle, _ptr(block_ids), int(K), _ptr(draft_ids),
+                                      _ptr(logits), _ptr(hidden), _stream(stream)))
 
 
 def dflash_step(ctx: Context, feats: Optional[torch.Tensor], n_new: Sequence[int], block_ids: torch.Tensor,
@@ -400,10 +458,11 @@ def dflash_step(ctx: Context, feats: Optional[torch.Tensor], n_new: Sequence[int
     if logits is not None and (logits.dtype != torch.float32 or
                                logits.numel() != ctx.batch * K * ctx.model.shape.vocab):
         raise ValueError("logits must be float32 [batch, K, vocab]")
-    _check("dflash_step",
-           lib.dflash_step(ctx.handle, _ptr(feats) if feats is not None and feats.numel() else None, nn,
-                           _ptr(block_ids), int(K), _ptr(draft_ids), _ptr(logits), _ptr(hidden),
-                           _stream(stream)))
+    with _on(stream):
+        _check("dflash_step",
+               lib.dflash_step(ctx.handle, _ptr(feats) if feats is not None and feats.numel() else None, nn,
+                               _ptr(block_ids), int(K), _ptr(draft_ids), _ptr(logits), _ptr(hidden),
+                               _stream(stream)))
 
 
 def dflash_accept(draft_ids: torch.Tensor, target_ids: torch.Tensor, batch: int, K: int,
@@ -466,9 +525,10 @@ def dflash_verify_block(ctx: Context, block_ids: torch.Tensor, K1: int, target_i
         raise ValueError("logits must be float32 [batch, K1, vocab]")
     if taps is not None and taps.numel() != ctx.batch * K1 * len(ctx.model.taps) * sh.hidden:
         raise ValueError("taps must be [batch, K1, n_taps * hidden]")
-    _check("dflash_verify_block",
-           lib.dflash_verify_block(ctx.handle, _ptr(block_ids), int(K1), _ptr(target_ids), _ptr(logits),
-                                   _ptr(taps), _stream(stream)))
+    with _on(stream):
+        _check("dflash_verify_block",
+               lib.dflash_verify_block(ctx.handle, _ptr(block_ids), int(K1), _ptr(target_ids), _ptr(logits),
+                                       _ptr(taps), _stream(stream)))
 
 
 def dflash_commit(ctx: Context, n_acc: Sequence[int], stream: Optional[torch.cuda.Stream] = None) -> None:
@@ -488,6 +548,7 @@ class AdaptPolicy:
         _check("dflash_adapt_create", lib.dflash_adapt_create(int(kmax), float(decay), float(min_count),
                                                               float(a0), float(gamma0), ctypes.byref(h)))
         self.handle = h
+        _LIVE.add(self)
 
     def observe(self, K: int, tau: int) -> None:
         _check("dflash_adapt_observe", lib.dflash_adapt_observe(self.handle, int(K), int(tau)))
@@ -509,6 +570,8 @@ class AdaptPolicy:
             self.handle = None
 
     def __del__(self):
+        if sys.is_finalizing():      # closed by the atexit hook, or torch is gone
+            return
         try:
             self.close()
         except Exception:

@@ -127,6 +127,45 @@ def test_small_bf16_l2_warm_up_settings(monkeypatch, warm):
     p.compare(_ids(44, 2, 16, SMALL.vocab))
 
 
+def test_side_stream_growth_and_draft():
+    """Every call on a non-default stream, with capacity growth (the library
+    frees the old buffers while the copy that reads them is still queued on
+    that stream) and torch allocating on its own stream meanwhile: the state
+    and the draft match the oracle."""
+    say("case: calls on a side stream with growth")
+    import block_diffusion_drafting_amd as dfl
+    p = Pair(SMALL, 47, 2, gain_std=0.1)
+    side = torch.cuda.Stream()
+    s = SMALL
+    feats0 = [synth.prefill_features(s, 47, b, n) for b, n in enumerate([60, 9])]
+    with torch.cuda.stream(side):
+        fd = to_dev(np.concatenate(feats0, axis=0))
+    dfl.dflash_project_ctx(p.ctx, fd, [60, 9], stream=side)
+    for b in range(2):
+        O.project_ctx(p.om, p.ost[b], feats0[b])
+    for t, n_new in enumerate([(5, 60), (70, 1)]):            # both sequences grow once
+        fe = [synth.step_features(s, 47, b, t, n) for b, n in enumerate(n_new)]
+        with torch.cuda.stream(side):
+            fd = to_dev(np.concatenate(fe, axis=0))
+        dfl.dflash_project_ctx(p.ctx, fd, list(n_new), stream=side)
+        junk = torch.randn(1 << 20, device="cuda")            # torch reuses memory on its own stream
+        del junk
+        for b in range(2):
+            O.project_ctx(p.om, p.ost[b], fe[b])
+    ids = _ids(48, 2, 16, s.vocab)
+    with torch.cuda.stream(side):
+        idd = to_dev(ids.astype(np.int32))
+        dr = torch.empty(2, 16, dtype=torch.int32, device="cuda")
+        lg = torch.empty(2, 16, s.vocab, dtype=torch.float32, device="cuda")
+    dfl.dflash_draft_block(p.ctx, idd, 16, dr, lg, stream=side)
+    side.synchronize()
+    p.check_state()
+    for b in range(2):
+        d_o, l_o, _ = p.oracle_draft(b, ids[b])
+        check_rows(f"logits[{b}]", lg.cpu().numpy()[b], l_o, tol(s))
+        check_argmax(dr.cpu().numpy()[b], l_o)
+
+
 def test_non_causal_through_abi():
     """Changing the last block token changes row 0's logits."""
     say("case: non-causal")
@@ -228,17 +267,20 @@ def test_accept_kernel_exhaustive_patterns():
         assert np.array_equal(out.cpu().numpy(), O.accept(d, t))
 
 
-def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=(), fused=False):
+def _session(shape, wl, steps, check_every=1, batch_seqs=None, tail_check=(), fused=False, keep_vocab=False):
     """GPU session and oracle session in lockstep; tau, ctx_len and cap must
     be identical every step; outputs compared on the checked steps.  With
     `fused`, the accepted positions of step t are appended by the
     dflash_step call that drafts step t + 1 (and by a final
     dflash_project_ctx), so the GPU state lags the oracle's by one append
-    between calls."""
+    between calls.  `keep_vocab` keeps the oracle's float64 LM head between
+    drafts (many sequences drafted per checked step)."""
     import block_diffusion_drafting_amd as dfl
     seqs = list(range(wl.batch)) if batch_seqs is None else batch_seqs
     w = _weights(shape, wl.seed)
     p = Pair(shape, wl.seed, wl.batch, weights=w, oracle_seqs=[])
+    if keep_vocab:
+        p.om.keep = True
     feats = [synth.prefill_features(shape, wl.seed, b, wl.ctx0[b]) for b in range(wl.batch)]
     p.project(feats)                      # GPU only: the oracle session prefills itself
     osess = O.Session(p.om, wl, keep_outputs=True, seqs=seqs)
@@ -410,15 +452,19 @@ def test_llama_shape_large_block(K):
 
 
 @pytest.mark.slow
-def test_workload4_batched_long_context_sampled():
-    """Batch 16, contexts 1k-32k: the GPU runs all 16 sequences; the oracle
-    follows two sampled sequences (the shortest and one mid-length) for the
-    whole session, compared at steps 0, 1 and the last."""
-    say("case: workload 4 sampled")
+@pytest.mark.timeout(600)
+def test_workload4_batched_long_context_all_sequences():
+    """Batch 16, contexts 1k-20k (171k positions in all): the GPU runs all
+    16 sequences in one ragged launch per kernel and the oracle follows
+    every one of them for the whole 32-step session.  After the prefill and
+    at the end, every sequence's context buffer and both caches of every
+    layer are compared; tau, ctx_len and cap of every sequence are exact at
+    every step; logits and argmax of all 16 sequences are compared at steps
+    0, 1 and 31 (the oracle advances without drafting in between: tau
+    depends only on the verifier's agreement draws)."""
+    say("case: workload 4, all 16 sequences")
     wl = synth.workload(4).replace(steps=32)
-    order = np.argsort(wl.ctx0)
-    seqs = sorted({int(order[0]), int(order[5])})
-    _session(wl.shape, wl, wl.steps, check_every=31, batch_seqs=seqs, tail_check=(1,))
+    _session(wl.shape, wl, wl.steps, check_every=31, tail_check=(1,), keep_vocab=True)
 
 
 _K_SWEEP = {}
