@@ -122,11 +122,23 @@ int32_t dflash_abi_version(void);
 /* Message for the last non-OK status returned on this thread. */
 const char *dflash_last_error(void);
 
-/* Validates the config, allocates model memory through `alloc` and repacks
+/* The drafter (kongchang.com, "D-Flash: diffusion drafting speeds LLM
+ * inference 3.5x", "System architecture": draft layers of bidirectional
+ * attention and an MLP, conditioned on a light projection of hidden states
+ * taken from several target layers, logits from the target's LM head;
+ * "Innovation 2: target-feature KV injection": that projection enters every
+ * layer through the layer's own K/V projections).
+ *   cfg    host, the shape; checked (DFLASH_E_ARG / DFLASH_E_SHAPE).
+ *   w      host struct of dev pointers in cfg->dtype (see dflash_weights).
+ *   alloc  host, the allocator for every model-owned buffer, or NULL.
+ *   out    host, receives the model handle (NULL on failure).
+ * Validates the config, allocates model memory through `alloc` and repacks
  * the weights into tiles laid out for gfx950 MFMA (a private copy; rows of
  * W_q/W_k are reordered to pair RoPE channels, W_gate/W_up are interleaved,
  * the per-layer W_k/W_v are stacked for context injection).  The repack runs
- * on `stream` and is complete when the call returns. */
+ * on `stream` and is complete when the call returns; on failure everything
+ * allocated is released.  dflash_model_destroy releases the model's memory
+ * (no context of it may be used afterwards; NULL is accepted). */
 dflash_status dflash_model_create(const dflash_config *cfg, const dflash_weights *w,
                                   const dflash_allocator *alloc, void *stream,
                                   dflash_model **out);
@@ -154,10 +166,23 @@ dflash_status dflash_target_create(const dflash_config *cfg, const dflash_weight
 dflash_status dflash_model_bytes(const dflash_model *m, int64_t *layer_bytes,
                                  int64_t *lm_head_bytes, int64_t *proj_bytes);
 
-/* Creates proposer state for `batch` sequences (1..DFLASH_MAX_BATCH).
- * init_cap: host [batch] powers of two, the initial context capacity of each
- * sequence, or NULL for capacity 0 (buffers are then created by the first
- * dflash_project_ctx).  All sequences start with ctx_len = 0. */
+/* Proposer state (Google Developers Blog, "Dual cache for attention": the
+ * drafter keeps a static, non-paged cache of its own beside the target's
+ * paged one; "Smart context management": a context buffer of power-of-two
+ * capacity that only newly accepted positions are appended to;
+ * "Bridging the metadata gap in TPU inference": the committed length and
+ * RoPE offset persist across steps).
+ * Creates proposer state for `batch` sequences (1..DFLASH_MAX_BATCH) of
+ * model m (which must outlive it).
+ *   init_cap  host [batch] powers of two, the initial context capacity of
+ *             each sequence, or NULL for capacity 0 (buffers are then
+ *             created by the first dflash_project_ctx); checked (E_ARG).
+ *   alloc     host, the allocator for every buffer the context owns, or NULL.
+ *   stream    the stream the initial buffer set-up is enqueued on.
+ *   out       host, receives the handle (NULL on failure).
+ * All sequences start with ctx_len = 0.  dflash_ctx_destroy releases every
+ * buffer through the allocator (work still queued on them must be on the
+ * stream the allocator orders reuse by; NULL is accepted). */
 dflash_status dflash_ctx_create(const dflash_model *m, int32_t batch, const int32_t *init_cap,
                                 const dflash_allocator *alloc, void *stream,
                                 dflash_ctx **out);
@@ -314,11 +339,19 @@ dflash_status dflash_adapt_observe(dflash_adapt *p, int32_t K, int32_t tau);
 dflash_status dflash_adapt_choose(const dflash_adapt *p, const int32_t *Ks, const double *cost, int32_t n,
                                   int32_t *K, double *a, double *gamma, double *tokens_per_cost);
 
-/* Host copies of the state: ctx_len and cap, host [batch] each (either may
- * be NULL). */
+/* Host copies of the state (Google Developers Blog, "Bridging the metadata
+ * gap in TPU inference": the host keeps the committed length that fixes
+ * the RoPE offset; "Smart context management": the power-of-two capacity):
+ * ctx_len and cap, host [batch] each, written by the call (either may be
+ * NULL).  No device work: the host values are authoritative and were
+ * updated when the last call was enqueued. */
 dflash_status dflash_ctx_query(const dflash_ctx *c, int32_t *ctx_len, int32_t *cap);
 
-/* Device buffers of sequence b (for tests and snapshots):
+/* Device buffers of sequence b (Google Developers Blog, "Dual cache for
+ * attention" and "Smart context management": the static cache and the
+ * context buffer; for tests and snapshots).  b in [0, batch), else E_ARG.
+ * Outputs are host pointers to write (any may be NULL); the buffers stay
+ * owned by the context:
  *   ctxbuf  [phys_rows, hidden] float32           projected features
  *   k_cache [n_layers, n_kv_heads, phys_rows, head_dim]   RoPE applied
  *   v_cache [n_layers, n_kv_heads, head_dim, phys_rows]   (transposed)
