@@ -74,7 +74,7 @@ class _Allocator(ctypes.Structure):
 EXPORTS = ("dflash_version", "dflash_abi_version", "dflash_last_error", "dflash_model_create",
            "dflash_model_destroy", "dflash_model_bytes", "dflash_ctx_create",
            "dflash_ctx_destroy", "dflash_project_ctx", "dflash_draft_block", "dflash_step",
-           "dflash_accept", "dflash_decay_ce", "dflash_target_create", "dflash_verify_block",
+           "dflash_accept", "dflash_decay_ce", "dflash_decay_ce_noalloc", "dflash_target_create", "dflash_verify_block",
            "dflash_commit", "dflash_adapt_create", "dflash_adapt_destroy", "dflash_adapt_observe",
            "dflash_adapt_choose",
            "dflash_ctx_query", "dflash_ctx_buffers", "dflash_ctx_set_persistent",
@@ -108,6 +108,8 @@ def _load() -> ctypes.CDLL:
         "dflash_accept": ([vp, vp, i32, i32, vp, vp], ctypes.c_int),
         "dflash_decay_ce": ([vp, ctypes.c_int, vp, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp, vp],
                             ctypes.c_int),
+        "dflash_decay_ce_noalloc": ([vp, ctypes.c_int, vp, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp],
+                                    ctypes.c_int),
         "dflash_target_create": ([ctypes.POINTER(_Config), ctypes.POINTER(_Weights), i32p,
                                   ctypes.POINTER(_Allocator), vp, ctypes.POINTER(vp)], ctypes.c_int),
         "dflash_verify_block": ([vp, vp, i32, vp, vp, vp, vp], ctypes.c_int),
@@ -508,6 +510,32 @@ def dflash_decay_ce(logits: torch.Tensor, targets: torch.Tensor, block: int, gam
            lib.dflash_decay_ce(_ptr(logits), dt, _ptr(targets), int(rows), int(vocab), int(block),
                                float(gamma), _ptr(loss), _ptr(ce), _ptr(grad), _ptr(workspace),
                                _stream(stream)))
+
+
+def dflash_decay_ce_noalloc(logits: torch.Tensor, targets: torch.Tensor, block: int, gamma: float,
+                            loss: torch.Tensor, ce: torch.Tensor, grad: Optional[torch.Tensor] = None,
+                            stream: Optional[torch.cuda.Stream] = None) -> None:
+    """dflash_decay_ce with the library's static per-GPU workspace: nothing
+    is allocated, here or in the library."""
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, vocab] tensor")
+    if logits.dtype == torch.bfloat16:
+        dt = DFLASH_BF16
+    elif logits.dtype == torch.float32:
+        dt = DFLASH_F32
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    rows, vocab = logits.shape
+    if targets.dtype != torch.int32 or targets.numel() != rows:
+        raise ValueError("targets must be int32 [rows]")
+    if loss.dtype != torch.float32 or loss.numel() < 1 or ce.dtype != torch.float32 or ce.numel() != rows:
+        raise ValueError("loss [1] and ce [rows] must be float32")
+    if grad is not None and (grad.dtype != logits.dtype or grad.shape != logits.shape or
+                             not grad.is_contiguous()):
+        raise ValueError("grad must match logits")
+    _check("dflash_decay_ce_noalloc",
+           lib.dflash_decay_ce_noalloc(_ptr(logits), dt, _ptr(targets), int(rows), int(vocab), int(block),
+                                       float(gamma), _ptr(loss), _ptr(ce), _ptr(grad), _stream(stream)))
 
 
 def dflash_verify_block(ctx: Context, block_ids: torch.Tensor, K1: int, target_ids: torch.Tensor,

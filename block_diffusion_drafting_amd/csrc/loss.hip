@@ -31,6 +31,9 @@
 #include <limits.h>
 #include <math.h>
 
+#include <cmath>
+#include <mutex>
+
 #include "../../include/dflash.h"
 #include "common.h"
 
@@ -457,3 +460,60 @@ hipError_t launch_decay_ce(const void* logits, int dtype, const int32_t* targets
 }
 
 }  // namespace dflash
+
+// ---------------------------------------------------------------------------
+// The same call for callers that cannot allocate (code under stream capture,
+// serving loops that forbid allocation): the weight sum lives in a
+// file-scope device array instead of a caller workspace.
+// ---------------------------------------------------------------------------
+// One copy per GPU, held until the process ends.  The kernels use one
+// double of it (the weight sum W, written by ce_scale_kernel before
+// ce_loss_kernel reads it on the same stream), whatever the rows and the
+// vocabulary, so no input size can exceed it.  Calls that overlap on one
+// GPU (different streams) race on it.
+static __device__ __align__(256) unsigned char scratch[DFLASH_DECAY_CE_WORKSPACE];
+static_assert(sizeof(double) <= DFLASH_DECAY_CE_WORKSPACE, "the weight sum must fit the scratch array");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch` per GPU (null until looked up)
+}  // namespace
+
+dflash_status dflash_set_error(dflash_status st, const char* msg);
+
+extern "C" dflash_status dflash_decay_ce_noalloc(const void* logits, dflash_dtype dtype, const int32_t* targets,
+                                                 int32_t rows, int32_t vocab, int32_t block, double gamma, float* loss,
+                                                 float* ce, void* grad, void* stream) {
+  using namespace dflash;
+  if (!loss) return dflash_set_error(DFLASH_E_ARG, "NULL pointer");
+  if (rows > 0 && (!logits || !targets || !ce)) return dflash_set_error(DFLASH_E_ARG, "NULL pointer");
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return dflash_set_error(DFLASH_E_ARG, "bad dtype");
+  if (rows < 0) return dflash_set_error(DFLASH_E_ARG, "rows < 0");
+  if (vocab < 1) return dflash_set_error(DFLASH_E_ARG, "vocab < 1");
+  if (block < 1) return dflash_set_error(DFLASH_E_ARG, "block < 1");
+  if (!(gamma > 0.0) || !std::isfinite(gamma)) return dflash_set_error(DFLASH_E_ARG, "gamma must be finite and > 0");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return dflash_set_error(DFLASH_E_HIP, "no current HIP device (or more than 64 devices)");
+  void* ptr = nullptr;
+  {
+    // once per GPU, with that GPU current: the array's device address (the
+    // array's name in host code is a host-side stand-in, never passed on)
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return dflash_set_error(DFLASH_E_HIP, "hipGetSymbolAddress of the decay-CE scratch array failed");
+      }
+      g_scratch_dev[dev] = p;
+    }
+    ptr = g_scratch_dev[dev];
+  }
+  const hipError_t e = launch_decay_ce(logits, (int)dtype, targets, rows, vocab, block, gamma, loss, ce,
+                                       rows > 0 ? grad : nullptr, (double*)ptr, (hipStream_t)stream);
+  if (e != hipSuccess) return dflash_set_error(DFLASH_E_HIP, hipGetErrorString(e));
+  return DFLASH_OK;
+}

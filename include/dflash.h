@@ -282,6 +282,22 @@ dflash_status dflash_decay_ce(const void *logits, dflash_dtype dtype, const int3
                               int32_t rows, int32_t vocab, int32_t block, double gamma, float *loss,
                               float *ce, void *grad, void *workspace, void *stream);
 
+/* dflash_decay_ce without the workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, serving loops and
+ * harnesses that forbid allocation): the library allocates nothing in this
+ * call.  The workspace is a file-scope device array of
+ * DFLASH_DECAY_CE_WORKSPACE bytes, one per GPU, held until the process
+ * ends; its device address is looked up on the first call on each GPU.
+ * The kernels use one double of it whatever rows and vocab are, so no input
+ * size exceeds it; other arguments, limits, results and errors as in
+ * dflash_decay_ce (the same kernels).  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams) race;
+ * calls ordered on one stream do not (each writes the slot before reading
+ * it).  Asynchronous on `stream`. */
+dflash_status dflash_decay_ce_noalloc(const void *logits, dflash_dtype dtype, const int32_t *targets,
+                                      int32_t rows, int32_t vocab, int32_t block, double gamma, float *loss,
+                                      float *ce, void *grad, void *stream);
+
 /* Target-side verification of a block of K1 rows per sequence: the anchor
  * (at position ctx_len) and the K1 - 1 drafts after it (Google Developers
  * Blog, "Overcoming the autoregressive bottleneck": one parallel forward of
