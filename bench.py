@@ -146,7 +146,8 @@ def persist_timeline(tr, n_layers):
     over layers), the median and slowest workgroup's time from the phase
     start to each mark inside it (1-5) and to its barrier arrival (6), and
     the barrier's latency from the last arrival to the first release."""
-    names = ["embed"] + [n for _ in range(n_layers) for n in ("qkv", "attention", "o_proj", "gate_up", "down")]
+    names = ["embed"] + [n for _ in range(n_layers) for n in ("qkv", "attention", "attn_merge", "o_proj", "gate_up",
+                                                              "down")]
     names.append("lm_head")
     tr = tr.astype(np.int64).reshape(tr.shape[0], -1, 8)
     acc = {}

@@ -156,8 +156,6 @@ struct dflash_ctx {
     bool enabled = false;   // opt in: measured slower than the per-product kernels
     int nwg = 0;            // workgroups (compute units); 0 = not probed yet, -1 = unavailable
     int down_splits = 8;
-    int pf_frags = 12;
-    int pf_att = 24;
     unsigned epoch = 0;     // launches since the barrier flags were last cleared
     int K = 0, max_splits = 0;   // shape the per-launch buffers were sized for
     Buf scratch;            // activations of every layer and phase (one launch)
@@ -765,8 +763,6 @@ static int persist_nwg(dflash_ctx* c) {
   auto& P = c->pst;
   if (P.nwg != 0) return P.nwg;
   P.nwg = -1;
-  P.pf_frags = env_int("DFLASH_PF_FRAGS", 12, 0, 48);
-  P.pf_att = env_int("DFLASH_PF_ATT", 2 * P.pf_frags, 0, 48);
   P.down_splits = env_int("DFLASH_DOWN_SPLITS", 8, 1, 32);
 
   int dev = 0, coop = 0, n = 0, occ = 0;
@@ -783,12 +779,15 @@ static int persist_nwg(dflash_ctx* c) {
 
 static bool persist_ok(dflash_ctx* c, int K) {
   const dflash_config& cf = c->m->cfg;
-  if (!c->pst.enabled || cf.dtype != DFLASH_BF16 || cf.n_layers < 1) return false;
+  if (!c->pst.enabled || cf.dtype != DFLASH_BF16 || cf.n_layers < 1 || cf.n_layers > PERSIST_MAX_LAYERS) return false;
   if ((int64_t)c->B * K > 16) return false;                       // one 16-row activation tile
   if ((int64_t)(cf.n_q_heads / cf.n_kv_heads) * K > 64) return false;  // one query group per KV head
   if (cf.head_dim != 64 && cf.head_dim != 128) return false;
   if (cf.hidden > 4096) return false;                              // norm loads per thread
-  return persist_nwg(c) > 0;
+  if (persist_nwg(c) <= 0) return false;
+  const dflash_model* m = c->m;
+  return persist_passes_fit(c->pst.nwg, c->pst.down_splits, cf.n_layers, m->qkv[0].n_tiles, m->o[0].n_tiles,
+                            m->gu[0].n_tiles, m->down[0].n_tiles, m->lm.n_tiles);
 }
 
 static dflash_status persist_draft(dflash_ctx* c, const int32_t* ids, int K, int32_t* draft, float* logits,
@@ -846,6 +845,7 @@ static dflash_status persist_draft(dflash_ctx* c, const int32_t* ids, int K, int
   const size_t o_lm = al(soff, 4);
   const size_t o_err = al(soff, 4);
   const size_t o_flags = al(soff, (size_t)nwg * 4);
+  const size_t o_zero = al(soff, BLOCK_BYTES);
   if (P.sync.bytes < soff || !P.sync.p) {
     if ((st = ensure(c->alloc, P.sync, soff))) return st;
     HIP_TRY(launch_fill_u32((unsigned*)P.sync.p, P.sync.bytes / 4, 0u, s));
@@ -882,8 +882,6 @@ static dflash_status persist_draft(dflash_ctx* c, const int32_t* ids, int K, int
   a.chunk = chunk;
   a.max_splits = max_splits;
   a.down_splits = S;
-  a.pf_frags = P.pf_frags;
-  a.pf_att = P.pf_att;
   a.xs = (float*)sb;
   a.xg = (u32x4*)(sb + o_xg);
   a.ssq = (float*)(sb + o_ssq);
@@ -900,6 +898,7 @@ static dflash_status persist_draft(dflash_ctx* c, const int32_t* ids, int K, int
   a.lmcnt = (unsigned*)(yb + o_lm);
   a.err = (unsigned*)(yb + o_err);
   a.flags = (unsigned*)(yb + o_flags);
+  a.zero_frag = yb + o_zero;
   a.base = P.epoch * persist_steps(L);
   if (c->prof.mask >> PH_PERSIST & 1u) {
     // timeline of this launch (profiling only)

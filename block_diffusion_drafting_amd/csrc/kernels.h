@@ -285,6 +285,8 @@ hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned v, hipStream_t s);
 // ---------------------------------------------------------------------------
 // persistent single-launch draft block (bf16 drafters, batch * K <= 16)
 // ---------------------------------------------------------------------------
+constexpr int PERSIST_MAX_LAYERS = 16;   // layers of a drafter the single launch takes
+
 struct PLayer {
   Packed qkv, o, gu, down;
   const float* attn_gain;
@@ -306,8 +308,6 @@ struct PArgs {
   float eps, scale_log2;
   int32_t chunk, max_splits; // attention: keys per split, splits per (sequence, head)
   int32_t down_splits;       // k-splits of the down projection (divides the grid)
-  int32_t pf_frags;          // warm-up fragments per wave share at a barrier
-  int32_t pf_att;            // the same at the barrier before attention
   // per-launch buffers, one copy per layer / phase (16 activation rows)
   float* xs;                 // [2L+1][16][H]          residual versions
   u32x4* xg;                 // [2L+1][hi, lo][H/32][64] normed-input frags
@@ -325,6 +325,7 @@ struct PArgs {
   unsigned* lmcnt;           // [1]
   unsigned* flags;           // [grid]      barrier flags (monotone)
   unsigned* err;             // nonzero: a wait expired
+  const uint8_t* zero_frag;  // one fragment (1 KiB) of zeros, never written
   unsigned base;             // flag value before this launch's first step
   // optional timeline (null = off): per workgroup, 8 slots per phase
   // (embed, 5 per layer, LM head) of the constant 100 MHz clock: [0] start,
@@ -335,6 +336,8 @@ struct PArgs {
 };
 // barrier steps of one launch with L layers
 unsigned persist_steps(int L);
+bool persist_passes_fit(int nwg, int down_splits, int L, int qkv_tiles, int o_tiles, int gu_tiles, int down_tiles,
+                        int lm_tiles);
 hipError_t persist_occupancy(int d, int* blocks_per_cu);
 hipError_t launch_persist_draft(const PArgs& a, int nwg, hipStream_t s);
 

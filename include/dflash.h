@@ -379,16 +379,20 @@ dflash_status dflash_ctx_buffers(const dflash_ctx *c, int32_t b, const void **ct
                                  const void **k_cache, const void **v_cache,
                                  int32_t *phys_rows);
 
-/* Single-launch draft block.  For bf16 drafters whose block has at most 16
- * rows in all (batch * K <= 16) and at most 64 query rows per KV head
- * ((n_q_heads / n_kv_heads) * K <= 64), dflash_draft_block runs a4-a9 as one
- * cooperative launch of one workgroup per compute unit, with the same
+/* Single-launch draft block.  For bf16 drafters of at most 16 layers whose
+ * block has at most 16 rows in all (batch * K <= 16) and at most 64 query
+ * rows per KV head ((n_q_heads / n_kv_heads) * K <= 64), and whose products
+ * split into at most 40 passes per workgroup, dflash_draft_block runs a4-a9
+ * as one cooperative launch of one workgroup per compute unit, with the same
  * arithmetic as the per-product kernels up to summation order (kongchang.com,
- * "System architecture": one forward per block; the launch keeps the weight
- * stream going across the dependencies between products).  Its grid
- * barriers wait at most about 2 s each; an expired wait abandons the launch
- * and is reported by dflash_ctx_check.  In dflash_step the appended
- * positions then go through dflash_project_ctx before the block.
+ * "System architecture": one forward per block).  In each workgroup four
+ * loader waves stream the weights of every product of the block, in order,
+ * into LDS rings that four compute waves consume, so the weight stream runs
+ * on across the dependencies between products.  Its grid barriers and ring
+ * waits end after about 2 s; an expired wait abandons the launch and is
+ * reported by dflash_ctx_check.  In dflash_step the appended positions then
+ * go through dflash_project_ctx before the block.  The path is slower than
+ * the per-product kernels on the shapes measured so far (off by default).
  *   dflash_ctx_set_persistent   enable or disable (default) the path for c;
  *                               the environment variable DFLASH_PERSISTENT=1
  *                               enables it for contexts created afterwards.
@@ -418,8 +422,10 @@ dflash_status dflash_profile_enable(dflash_ctx *c, uint32_t phase_mask);
 /* Timeline of the last single-launch draft block run while phase 15 was
  * selected: *nwg workgroups x *stride slots (host out [nwg * stride] uint64,
  * capacity entries), ticks of the GPU's constant 100 MHz clock per
- * workgroup, 8 slots per phase (embed, then qkv, attention, o_proj, gate_up,
- * down per layer, then lm_head): 0 start, 1-5 marks inside the phase, 6
+ * workgroup, 8 slots per phase (embed, then qkv, attention, attention merge,
+ * o_proj, gate_up, down per layer, then lm_head): 0 start, 1-5 marks inside
+ * the phase (2 first pass's product done, 3 its sums and epilogue done, 4
+ * all passes done), 6
  * arrival at the barrier that ends it (lm_head: end of work), 7 release;
  * unwritten slots are 0.  *nwg = 0 if none was recorded; out = NULL only returns the sizes.
  * Waits for the device. */
