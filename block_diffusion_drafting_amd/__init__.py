@@ -228,9 +228,9 @@ class TorchAllocator:
         self.live[p] = t
         return p
 
-    def _free(self, p: int, user) -> None:
+    def _free(self, p: int, user, _finalizing=sys.is_finalizing) -> None:
         t = self.live.pop(int(p) if p else 0, None)
-        if t is not None and not sys.is_finalizing():
+        if t is not None and not _finalizing():
             # work queued on the freeing call's stream (torch's current stream
             # during the call) may still use the block: torch reuses it only
             # after that work, also when it was allocated on another stream
@@ -310,8 +310,9 @@ class Model:
             lib.dflash_model_destroy(self.handle)
             self.handle = None
 
-    def __del__(self):
-        if sys.is_finalizing():      # closed by the atexit hook, or torch is gone
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # (bound at definition: module globals may already be None at exit)
+        if _finalizing():            # closed by the atexit hook, or torch is gone
             return
         try:
             self.close()
@@ -413,8 +414,9 @@ class Context:
             lib.dflash_ctx_destroy(self.handle)
             self.handle = None
 
-    def __del__(self):
-        if sys.is_finalizing():      # closed by the atexit hook, or torch is gone
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # (bound at definition: module globals may already be None at exit)
+        if _finalizing():            # closed by the atexit hook, or torch is gone
             return
         try:
             self.close()
@@ -597,8 +599,9 @@ class AdaptPolicy:
             lib.dflash_adapt_destroy(self.handle)
             self.handle = None
 
-    def __del__(self):
-        if sys.is_finalizing():      # closed by the atexit hook, or torch is gone
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # (bound at definition: module globals may already be None at exit)
+        if _finalizing():            # closed by the atexit hook, or torch is gone
             return
         try:
             self.close()

@@ -136,14 +136,12 @@ struct dflash_ctx {
   DevSeq* seq_dev = nullptr;
   // workspaces
   Buf x, ssq, q, bk, bvt, keys, part, attn_part, rowmap;
+  Buf fixcnt;   // arrival counters of split-K products (zero between launches)
   Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
-  // L2 warm-up by the spare blocks of latency-bound kernels (fragments per
-  // product wave): output projection, next QKV, LM head.  Measured on the
-  // Qwen3-4B-shaped K = 16 step: the output projection's warm-up pays (its
-  // whole weight set, from the attention kernel); those of the next QKV and
-  // of the LM head (from the residual pass) now cost the residual pass more
-  // than they save, so they are off by default.
-  int warm_o = 16, warm_qkv = 0, warm_lm = 0;
+  // L2 warm-up of the output projection's weights by spare blocks of the
+  // attention kernel (fragments per product wave; measured on the
+  // Qwen3-4B-shaped K = 16 step: its whole weight set pays)
+  int warm_o = 16;
   // attention grid: 8-wave workgroup equivalents per compute unit, and the
   // shortest key split (a multiple of 64)
   int attn_wgs_per_cu = 2;
@@ -514,8 +512,6 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
   c->seq.assign(batch, DevSeq{});
   c->pst.enabled = env_int("DFLASH_PERSISTENT", 0, 0, 1) != 0;
   c->warm_o = env_int("DFLASH_WARM_O", c->warm_o, 0, 64);
-  c->warm_qkv = env_int("DFLASH_WARM_QKV", c->warm_qkv, 0, 64);
-  c->warm_lm = env_int("DFLASH_WARM_LM", c->warm_lm, 0, 64);
   c->attn_wgs_per_cu = env_int("DFLASH_ATTN_WGS_PER_CU", c->attn_wgs_per_cu, 1, 16);
   c->attn_min_split = round_up(env_int("DFLASH_ATTN_MIN_SPLIT", c->attn_min_split, 64, 1 << 20), 64);
   c->attn_stream_mb = env_int("DFLASH_ATTN_STREAM_MB", c->attn_stream_mb, 0, 1 << 20);
@@ -552,7 +548,7 @@ dflash_status dflash_ctx_destroy(dflash_ctx* c) {
     c->alloc.put(v.vt);
   }
   c->alloc.put(c->seq_dev);
-  for (Buf* b : {&c->x, &c->ssq, &c->q, &c->bk, &c->bvt, &c->keys, &c->part, &c->attn_part, &c->rowmap,
+  for (Buf* b : {&c->x, &c->ssq, &c->q, &c->bk, &c->bvt, &c->keys, &c->part, &c->attn_part, &c->rowmap, &c->fixcnt,
                  &c->xg_hi, &c->xg_lo, &c->o_hi, &c->o_lo, &c->act_hi, &c->act_lo, &c->c_hi, &c->c_lo,
                  &c->pst.scratch, &c->pst.apart, &c->pst.sync, &c->pst.trace})
     c->alloc.put(b->p);
@@ -618,6 +614,17 @@ static dflash_status run_gemm(dflash_ctx* c, int phase, int epi, const Packed& W
   e.part = (float*)c->part.p;
   e.part_ntiles = W.n_tiles;
   e.part_mtiles = (M + 15) / 16;
+  if (epi == EPI_PARTRES) {
+    if (p.nsplit > MAX_SPLITS) return fail(DFLASH_E_ARG, "split product: %d splits", p.nsplit);
+    // one counter per (tile group, m-group), zero-filled when allocated;
+    // every launch leaves its counters at zero
+    const size_t bytes = (size_t)p.n_groups * p.m_groups * sizeof(unsigned);
+    if (c->fixcnt.bytes < bytes || !c->fixcnt.p) {
+      if ((st = ensure(c->alloc, c->fixcnt, bytes))) return st;
+      HIP_TRY(launch_fill_u32((unsigned*)c->fixcnt.p, c->fixcnt.bytes / 4, 0u, s));
+    }
+    e.fix_cnt = (unsigned*)c->fixcnt.p;
+  }
   {
     PhaseTimer tm(c, phase, s);
     HIP_TRY(launch_gemm<T>(epi, p, g, e, s));
@@ -1065,7 +1072,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
     }
     a.layer = l;
     // the attention kernel's spare blocks warm the output projection's weights
-    a.warm = make_warm<T>(mtiles == 1 ? EPI_RESNORM : EPI_PART, m->o[l], M, c->warm_o);
+    a.warm = make_warm<T>(mtiles == 1 ? EPI_RESNORM : mtiles <= 4 ? EPI_PARTRES : EPI_PART, m->o[l], M, c->warm_o);
     {
       PhaseTimer tm(c, PH_ATTN, s);
       HIP_TRY(launch_attention<CT>(a, s));
@@ -1074,42 +1081,53 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
       PhaseTimer tm(c, PH_COMBINE, s);
       HIP_TRY((launch_attn_combine<CT, T>(a, of, s)));
     }
-    GemmPlan p;
+    // The output projection and the down projection add into the residual
+    // and write the next norm's inputs (x * gain in frag layout, sums of
+    // squares): for one m-tile the output projection runs over the whole
+    // reduction with that epilogue (EPI_RESNORM); the split products of up
+    // to four m-tiles end with their last split adding the partials
+    // (EPI_PARTRES, sums of squares per 16 columns); with more rows a tile
+    // group's partials are too many for one workgroup, and a residual pass
+    // over the whole grid adds them (sums of squares per 64 columns).
+    // Measured on the Qwen3-4B shape: down at K = 16 11.6 + 4.8 -> 15.1 us
+    // per layer with EPI_PARTRES; at K = 128 (eight m-tiles) EPI_PARTRES
+    // was 0.10 ms per block slower than the residual pass.
+    const bool fix = mtiles <= 4;
+    EpiArgs eo = e;
+    eo.xres = (float*)c->x.p;
+    eo.gain = m->mlp_gain(l);
+    eo.xout = xg;
+    eo.ssq_out = (float*)c->ssq.p;
     EpiArgs eg = e;
-    if (mtiles == 1) {
-      // one m-tile: the output projection runs over the whole reduction and
-      // its epilogue adds into the residual and writes the MLP norm's
-      // inputs (sums of squares per 16 columns), so no residual pass runs
-      // (with more rows the split form is faster)
-      EpiArgs eo = e;
-      eo.xres = (float*)c->x.p;
-      eo.gain = m->mlp_gain(l);
-      eo.xout = xg;
-      eo.ssq_out = (float*)c->ssq.p;
-      if ((st = run_gemm<T>(c, PH_O, EPI_RESNORM, m->o[l], of, nullptr, 0, M, eo, s))) return st;
+    GemmPlan p;
+    if (mtiles == 1 || fix) {
+      if ((st = run_gemm<T>(c, PH_O, mtiles == 1 ? EPI_RESNORM : EPI_PARTRES, m->o[l], of, nullptr, 0, M, eo, s)))
+        return st;
       eg.ssq_groups = H / 16;
     } else {
       if ((st = run_gemm<T>(c, PH_O, EPI_PART, m->o[l], of, nullptr, 0, M, e, s, &p))) return st;
       PhaseTimer tm(c, PH_RESID, s);
       HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
                                    m->mlp_gain(l), xg, (float*)c->ssq.p, s));
+      eg.ssq_groups = G;
     }
     if ((st = run_gemm<T>(c, PH_GU, EPI_SWIGLU, m->gu[l], xg, nullptr, 0, M, eg, s))) return st;
-    if ((st = run_gemm<T>(c, PH_DOWN, EPI_PART, m->down[l], af, nullptr, 0, M, e, s, &p))) return st;
-    {
+    EpiArgs ed = eo;
+    ed.gain = l + 1 < L ? m->attn_gain(l + 1) : m->final_gain();
+    if (fix) {
+      if ((st = run_gemm<T>(c, PH_DOWN, EPI_PARTRES, m->down[l], af, nullptr, 0, M, ed, s))) return st;
+      e.ssq_groups = H / 16;   // the next layer's QKV, the LM head and the final norm
+    } else {
+      if ((st = run_gemm<T>(c, PH_DOWN, EPI_PART, m->down[l], af, nullptr, 0, M, e, s, &p))) return st;
       PhaseTimer tm(c, PH_RESID, s);
-      // and the next product's weights (the next layer's QKV, or the LM head)
-      const Warm wn = l + 1 < L ? make_warm<T>(EPI_QKV, m->qkv[l + 1],
-                                               fused.n_ctx > 0 ? fused.mt0 * 16 + fused.n_ctx : M, c->warm_qkv)
-                                : make_warm<T>(EPI_ARGMAX, m->lm, M, c->warm_lm);
-      HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p,
-                                   l + 1 < L ? m->attn_gain(l + 1) : m->final_gain(), xg, (float*)c->ssq.p, s,
-                                   wn));
-      if (vo.on && vo.taps) {
-        const int nt = (int)m->taps.size();
-        for (int ti = 0; ti < nt; ++ti)
-          if (m->taps[ti] == l) HIP_TRY(launch_tap<T>((const float*)c->x.p, M, H, ti, nt, vo.taps, s));
-      }
+      HIP_TRY(launch_resid_norm<T>((const float*)c->part.p, p.nsplit, mtiles, M, H, (float*)c->x.p, ed.gain, xg,
+                                   (float*)c->ssq.p, s));
+      e.ssq_groups = G;
+    }
+    if (vo.on && vo.taps) {
+      const int nt = (int)m->taps.size();
+      for (int ti = 0; ti < nt; ++ti)
+        if (m->taps[ti] == l) HIP_TRY(launch_tap<T>((const float*)c->x.p, M, H, ti, nt, vo.taps, s));
     }
   }
   (void)none;

@@ -30,7 +30,7 @@ constexpr int kCUs = 256;
 // 1024 630 -> 500 us per block with eight; at eight m-groups, 512 rows,
 // eight was slower).
 static int max_ntg(int mtt, int epi, int m_groups) {
-  if (mtt == 8) return epi == EPI_PART ? 5 : 4;
+  if (mtt == 8) return is_part(epi) ? 5 : 4;
   if (mtt == 4) return epi == EPI_QKV && m_groups >= 16 ? 8 : 5;
   return 8;
 }
@@ -79,7 +79,7 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
   // kernel takes it (K = 128 314 -> 240 us, batch 16 600 -> 517 us; 32-row
   // groups slower); the k-split products (o, down) in 32-row groups up to
   // 64 rows (K = 64 214 -> 175 us; slower in 64-row groups at 128 rows).
-  if (p.split && ((epi == EPI_QKV && mtiles <= 8) || (epi == EPI_PART && mtiles <= 4)) && mtiles > 2) {
+  if (p.split && ((epi == EPI_QKV && mtiles <= 8) || (is_part(epi) && mtiles <= 4)) && mtiles > 2) {
     p.mtt = 2;
     p.m_groups = (mtiles + 1) / 2;
   } else if (p.split && p.mtt == 8 &&
@@ -89,8 +89,8 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
     p.m_groups = (mtiles + 3) / 4;
   }
   const int T = W.n_tiles;
-  if (epi == EPI_PART) {
-    int ns = 8;
+  if (is_part(epi)) {
+    int ns = MAX_SPLITS;
     while (ns > 1 && W.nkb / ns < 8) ns /= 2;
     p.kbu = (W.nkb + ns - 1) / ns;
     p.nsplit = (W.nkb + p.kbu - 1) / p.kbu;
@@ -126,6 +126,7 @@ hipError_t launch_gemm(int epi, const GemmPlan& p, const GemmArgs& g, const EpiA
     case EPI_FC: return launch_gemm_epi<T, EPI_FC>(p, g, e, s);
     case EPI_KV: return launch_gemm_epi<T, EPI_KV>(p, g, e, s);
     case EPI_RESNORM: return launch_gemm_epi<T, EPI_RESNORM>(p, g, e, s);
+    case EPI_PARTRES: return launch_gemm_epi<T, EPI_PARTRES>(p, g, e, s);
   }
   return hipErrorInvalidValue;
 }

@@ -11,10 +11,11 @@
 //   * the four partial sums are added through LDS in wave order and the
 //     epilogue runs on complete sums inside the workgroup;
 //   * nothing in a launch waits for another workgroup: products split over
-//     k across workgroups (EPI_PART) write their partial tiles with plain
-//     stores, and the next kernel adds them in split order.  Results are
-//     therefore deterministic, and no device-scope fence (an L2 writeback +
-//     invalidate on this GPU) is ever executed.
+//     k across workgroups write their partial tiles, and either the next
+//     kernel (EPI_PART) or the last split of each tile group to finish
+//     (EPI_PARTRES, counted by an agent-scope atomic) adds them in split
+//     order.  Results are therefore deterministic, and no device-scope
+//     fence (an L2 writeback + invalidate on this GPU) is ever executed.
 // Rows of the activation matrix beyond M are computed but never stored.
 #pragma once
 
@@ -45,6 +46,24 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)hi << 32) | lo;
 }
 
+// Device-scope (write-through) store and load of four floats: data passed
+// between workgroups of one launch, which may sit on different XCDs (each
+// with its own L2).
+__device__ __forceinline__ void store_agent_f32x4(float* p, f32x4 v) {
+  typedef __attribute__((address_space(1))) unsigned long long g_u64;
+  __hip_atomic_store((g_u64*)p, (unsigned long long)__float_as_uint(v[0]) | ((unsigned long long)__float_as_uint(v[1]) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((g_u64*)(p + 2), (unsigned long long)__float_as_uint(v[2]) | ((unsigned long long)__float_as_uint(v[3]) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_agent_f32x4(const float* p) {
+  typedef __attribute__((address_space(1))) unsigned long long g_u64;
+  const unsigned long long a = __hip_atomic_load((g_u64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load((g_u64*)(p + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
+               __uint_as_float((uint32_t)(b >> 32))};
+}
+
 // Context K/V rows: nn = offset inside one layer's [K rows | V rows] block
 // (K rows in RoPE pair order), row map rm of the context row, values acc.
 template <typename CT>
@@ -73,6 +92,47 @@ __device__ __forceinline__ void store_ctx_kv(const EpiArgs& e, int l, int nn, co
   }
 }
 
+// Residual epilogue of one output tile (EPI_RESNORM, EPI_PARTRES): lane
+// (g4, r) owns x[m][n..n+3] with m = mt*16 + r, n = tile*16 + 4*g4.  Its
+// inputs (the residual quad and the next norm's gain) are loaded apart, so
+// that they can be in flight with the loads of the sums.
+struct ResIn {
+  f32x4 x, gn;
+};
+__device__ __forceinline__ ResIn resnorm_load(const EpiArgs& e, int tile, int mt, int lane) {
+  const int m = mt * 16 + (lane & 15), n = tile * 16 + (lane >> 4) * 4;
+  ResIn r{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (m < e.M) {
+    r.x = *gp((const f32x4*)(e.xres + (size_t)m * e.H + n));
+    r.gn = gld((const f32x4*)(e.gain + n));
+  }
+  return r;
+}
+// x += y; x * gain -> frag; sum of squares of the tile's 16 columns of row
+// m (all lanes take part in the reduction)
+template <typename T>
+__device__ __forceinline__ void resnorm_tile(const EpiArgs& e, int tile, int mt, f32x4 acc, int lane,
+                                             const ResIn& in) {
+  const int g4 = lane >> 4;
+  const int m = mt * 16 + (lane & 15), n = tile * 16 + g4 * 4;
+  const bool ok = m < e.M;
+  float ss = 0.f;
+  if (ok) {
+    const f32x4 x = in.x + acc;
+    *gp((f32x4*)(e.xres + (size_t)m * e.H + n)) = x;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ss = fmaf(x[j], x[j], ss);
+      v[j] = x[j] * in.gn[j];
+    }
+    frag_store<T, 4>(e.xout, m, n, v);
+  }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  if (ok && g4 == 0) e.ssq_out[(size_t)tile * e.M + m] = ss;
+}
+
 // One complete 16x16 output tile: acc[j] is output row n = tile*16 +
 // 4*(lane/16) + j of activation row m = mt*16 + lane%16.  Runs on one wave.
 template <typename T, int EPI>
@@ -82,32 +142,19 @@ __device__ void epilogue_tile(const EpiArgs& e, int s, int tile, int mt, f32x4 a
   const int g4 = lane >> 4;
   const int m = mt * 16 + (lane & 15);
   if constexpr (EPI == EPI_RESNORM) {
-    // x[m][n..n+3] += y; x * gain -> frag; sum of squares of the tile's 16
-    // columns of row m (all lanes take part in the reduction)
-    const int n = tile * 16 + g4 * 4;
-    const bool ok = m < e.M;
-    float ss = 0.f;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      auto xp = gp((f32x4*)(e.xres + (size_t)m * e.H + n));
-      f32x4 x = *xp + acc;
-      *xp = x;
-      const f32x4 gn = gld((const f32x4*)(e.gain + n));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ss = fmaf(x[j], x[j], ss);
-        v[j] = x[j] * gn[j];
-      }
-      frag_store<T, 4>(e.xout, m, n, v);
-    }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    if (ok && g4 == 0) e.ssq_out[(size_t)tile * e.M + m] = ss;
+    resnorm_tile<T>(e, tile, mt, acc, lane, resnorm_load(e, tile, mt, lane));
     return;
   }
   if constexpr (EPI == EPI_PART) {
     if (mt >= e.part_mtiles) return;   // m-tile past the rows of the call: no slot
     *gp((f32x4*)(e.part + ((((size_t)s * e.part_ntiles + tile) * e.part_mtiles + mt) * 64 + lane) * 4)) = acc;
+    return;
+  }
+  if constexpr (EPI == EPI_PARTRES) {
+    // write-through: another XCD's workgroup adds the partials in this launch
+    if (mt >= e.part_mtiles) return;
+    float* p = e.part + ((((size_t)s * e.part_ntiles + tile) * e.part_mtiles + mt) * 64 + lane) * 4;
+    store_agent_f32x4(p, acc);
     return;
   }
   if constexpr (EPI == EPI_QKV) {
@@ -444,6 +491,47 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
       if (m < e.M && k) atomicMax(e.keys + m, k);
     }
   }
+  if constexpr (EPI == EPI_PARTRES) {
+    // Arrival of this split of the tile group (ng, mg): every wave's partial
+    // stores have completed (waited for, write-through) before one atomic
+    // increment at agent scope.  The split that brings the count to nsplit
+    // resets it (for the next launch) and adds the group's partials, split 0
+    // first, then runs the residual epilogue on the sums.  No workgroup
+    // waits for another.
+    __shared__ unsigned is_last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      typedef __attribute__((address_space(1))) unsigned g_u32;
+      g_u32* cnt = (g_u32*)(e.fix_cnt + (size_t)ng * g.m_groups + mg);
+      const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned last = old + 1u == (unsigned)g.nsplit ? 1u : 0u;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      is_last = last;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    // every load of a tile (the partials of all splits, the residual quad
+    // and the gain) is issued before the first is used: a split past
+    // nsplit re-reads the last one, which is not added
+    const size_t sstride = (size_t)e.part_ntiles * e.part_mtiles * 64 * 4;   // floats between splits
+    for (int it = wave; it < nt * MTT; it += WAVES) {
+      const int tile = tile0 + it / MTT, mt = mt0 + it % MTT;
+      if (mt >= e.part_mtiles) continue;   // uniform over the wave
+      const float* p = e.part + (((size_t)tile * e.part_mtiles + mt) * 64 + lane) * 4;
+      f32x4 pv[MAX_SPLITS];
+#pragma unroll
+      for (int sp = 0; sp < MAX_SPLITS; ++sp) pv[sp] = load_agent_f32x4(p + min(sp, g.nsplit - 1) * sstride);
+      const ResIn in = resnorm_load(e, tile, mt, lane);
+      f32x4 sum = pv[0];
+#pragma unroll
+      for (int sp = 1; sp < MAX_SPLITS; ++sp)
+        if (sp < g.nsplit) sum += pv[sp];
+      resnorm_tile<T>(e, tile, mt, sum, lane, in);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -505,7 +593,7 @@ inline hipError_t launch_mtt(const GemmPlan& p, const GemmArgs& g, const EpiArgs
       case 2: return launch_h<T, MTT, 2, EPI, ROW, SPLIT>(p, g, e, s);
       case 4: return launch_h<T, MTT, 4, EPI, ROW, SPLIT>(p, g, e, s);
     }
-    if constexpr (MTT <= 4 || EPI == EPI_PART) {
+    if constexpr (MTT <= 4 || is_part(EPI)) {
       if (p.ntg == 5) return launch_h<T, MTT, 5, EPI, ROW, SPLIT>(p, g, e, s);
     }
     if constexpr (MTT <= 2 || (MTT == 4 && EPI == EPI_QKV)) {

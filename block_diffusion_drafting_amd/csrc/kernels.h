@@ -29,7 +29,12 @@ enum Epi : int {
   EPI_RESNORM = 6, // full-K product added into the residual x; the next
                    // RMSNorm's inputs (x * gain -> frag, sums of squares per
                    // 16 columns) written alongside
+  EPI_PARTRES = 7, // split-K partial tiles; the last split of a tile group
+                   // to finish adds the group's partials in split order and
+                   // runs the EPI_RESNORM epilogue on the sums
 };
+constexpr bool is_part(int epi) { return epi == EPI_PART || epi == EPI_PARTRES; }
+constexpr int MAX_SPLITS = 8;   // k-splits of a split product (plan_gemm)
 
 // A weight matrix repacked into 16-row x 64-byte blocks (see common.h):
 // tile t (rows 16t..16t+15) holds nkb consecutive 1 KiB blocks.
@@ -85,6 +90,9 @@ struct EpiArgs {
   const float* gain;
   Frag xout;
   float* ssq_out;
+  // EPI_PARTRES: arrival counters, one per (tile group, m-group) of the
+  // launch, zero before it and left zero by it
+  unsigned* fix_cnt;
 };
 
 struct GemmArgs {
@@ -237,10 +245,6 @@ hipError_t launch_embed(const int32_t* ids, const void* embed, const float* gain
                         int V, float* x, Frag xg, float* ssq, unsigned long long* keys,
                         hipStream_t s);
 // x += sum of split-K partials (fixed order); xg = x * gain -> frag; ssq.
-template <typename T>
-hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
-                             const float* gain, Frag xg, float* ssq, hipStream_t s,
-                             const Warm& warm = Warm{});
 // Rows of one context append: rows [start[b], start[b+1]) belong to
 // sequence b and go to slots ctx0[b] + (row - start[b]) (host values).
 struct RowInfo {
@@ -256,6 +260,9 @@ hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, 
                               int row0, hipStream_t s);
 // out[m][tap*H + h] = x[m][h] in the model type (a tapped hidden state;
 // out rows are n_taps*H long).
+template <typename T>
+hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
+                             const float* gain, Frag xg, float* ssq, hipStream_t s);
 template <typename T>
 hipError_t launch_tap(const float* x, int M, int H, int tap, int n_taps, void* out, hipStream_t s);
 // draft ids from argmax keys; optional final-normed hidden rows.

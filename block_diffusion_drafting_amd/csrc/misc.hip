@@ -87,18 +87,8 @@ __device__ __forceinline__ f32x4 sum_parts(const float* part, int nsplit, int nt
 template <typename T>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* part, int nsplit, int mtiles,
                                                          int M, int H, float* x,
-                                                         const float* gain, Frag xg, float* ssq,
-                                                         Warm warm) {
-  // appended workgroups warm the next product's weights (see Warm)
-  if (warm.w && (int)blockIdx.x >= warm.first) {
-    __shared__ __attribute__((aligned(1024))) uint8_t slot[4][1024];
-    warm_consumer(warm, (int)blockIdx.x - warm.first, 4, (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63),
-                  (lds_void_t*)slot[threadIdx.x >> 6]);
-    return;
-  }
-  // block b: m-tile b % mtiles, 64-column group b / mtiles; the blocks that
-  // pad the grid to a multiple of 8 before the warm-up blocks do nothing
-  if ((int)blockIdx.x >= mtiles * (H / 64)) return;
+                                                         const float* gain, Frag xg, float* ssq) {
+  // block b: m-tile b % mtiles, 64-column group b / mtiles
   const int mtile = (int)blockIdx.x % mtiles, cgrp = (int)blockIdx.x / mtiles;
   const int m = mtile * 16 + (threadIdx.x >> 4);
   const int n0 = cgrp * 64 + (threadIdx.x & 15) * 4;
@@ -123,22 +113,16 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* part, int 
 
 template <typename T>
 hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
-                             const float* gain, Frag xg, float* ssq, hipStream_t s, const Warm& warm_in) {
-  Warm warm = warm_in;
-  unsigned nblk = (unsigned)(mtiles * (H / 64));
-  if (warm.w) {
-    nblk = (nblk + 7u) / 8u * 8u;
-    warm.first = (int)nblk;
-    nblk += (unsigned)warm.consumers;
-  }
+                             const float* gain, Frag xg, float* ssq, hipStream_t s) {
+  const unsigned nblk = (unsigned)(mtiles * (H / 64));
   hipLaunchKernelGGL((resid_norm_kernel<T>), dim3(nblk), dim3(256), 0, s, part, nsplit, mtiles, M, H, x,
-                     gain, xg, ssq, warm);
+                     gain, xg, ssq);
   return hipGetLastError();
 }
 template hipError_t launch_resid_norm<bf16_t>(const float*, int, int, int, int, float*, const float*,
-                                              Frag, float*, hipStream_t, const Warm&);
+                                              Frag, float*, hipStream_t);
 template hipError_t launch_resid_norm<float>(const float*, int, int, int, int, float*, const float*,
-                                             Frag, float*, hipStream_t, const Warm&);
+                                             Frag, float*, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // (a1)-(a2) context projection split over k: c = sum_s part_s, written to

@@ -412,8 +412,10 @@ dflash_status dflash_ctx_check(dflash_ctx *c, void *stream);
  * p; 0 turns timing off; bits past the last phase are ignored).
  * Phases (index: name): 0 embed, 1 qkv, 2 attention, 3 o_proj, 4 gate_up,
  * 5 down, 6 lm_head, 7 finalize, 8 fc, 9 kv_inject, 10 grow, 11 rowmap,
- * 12 attn_combine, 13 resid_norm, 14 fc_finalize, 15 persistent_draft (the
- * whole draft block as one launch, see dflash_ctx_set_persistent).
+ * 12 attn_combine, 13 resid_norm (blocks of more than 64 rows; smaller
+ * ones add into the residual in the products' epilogue), 14 fc_finalize,
+ * 15 persistent_draft (the whole draft block as one launch, see
+ * dflash_ctx_set_persistent).
  * dflash_profile_read waits for the recorded events, adds their durations
  * (milliseconds) and launch counts per phase into ms[] / count[] (host
  * arrays of DFLASH_NUM_PHASES entries, overwritten) and clears the record. */
