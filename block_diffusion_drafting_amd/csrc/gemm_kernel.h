@@ -342,27 +342,43 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
   for (int t = 0; t < NTG; ++t)
 #pragma unroll
     for (int mt = 0; mt < MTT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the norm scale of this workgroup's rows, loaded while the weights
-  // stream: thread (part p, row r) adds groups p, p + P, ... of row r; the
-  // P parts are then added in order
-  if constexpr (needs_norm(EPI)) {
-    constexpr int R = MTT * 16, P = WAVES * 64 / R;
-    __shared__ float npart[P][R];
-    const int r = threadIdx.x % R, part = threadIdx.x / R;
-    const int m = mt0 * 16 + r;
-    float sum = 0.f;
-    if (m < e.M) {
-#pragma unroll 4
-      for (int g = part; g < e.ssq_groups; g += P) sum += e.ssq[(size_t)g * e.M + m];
-    }
-    npart[part][r] = sum;
+  // The norm scale of this workgroup's rows: thread (part p, row r) adds
+  // groups p, p + P, ... of row r, then the P parts are added in order.
+  // With one or two m-tiles the thread's first NPRE groups (all of them up
+  // to 4096 columns) are loaded here, before the first weight batch, from
+  // in-range addresses whatever the row (so no load waits on a branch),
+  // and added after the main loop: the weights start streaming at once.
+  // With more rows the sum is formed here, before the main loop.
+  constexpr int NR = MTT * 16, NP = WAVES * 64 / NR;
+  constexpr int NPRE = (needs_norm(EPI) && MTT <= 2) ? 256 / NP : 0;
+  __shared__ float npart[NP][NR];
+  float npre[NPRE > 0 ? NPRE : 1];
+  const int nr = threadIdx.x % NR, npt = threadIdx.x / NR;
+  const int nm = mt0 * 16 + nr;
+  auto norm_finish = [&](float sum) {
+    npart[npt][nr] = sum;
     __syncthreads();
-    if (threadIdx.x < R) {
+    if (threadIdx.x < NR) {
       float t = 0.f;
 #pragma unroll
-      for (int q = 0; q < P; ++q) t += npart[q][threadIdx.x];
-      rnorm[threadIdx.x] = m < e.M ? rsqrtf(t / (float)e.norm_dim + e.eps) : 0.f;
+      for (int q = 0; q < NP; ++q) t += npart[q][threadIdx.x];
+      rnorm[threadIdx.x] = nm < e.M ? rsqrtf(t / (float)e.norm_dim + e.eps) : 0.f;
     }
+  };
+  if constexpr (NPRE > 0) {
+    const int mc = min(nm, e.M - 1);
+#pragma unroll
+    for (int j = 0; j < NPRE; ++j) {
+      const int gi = npt + j * NP;
+      npre[j] = e.ssq[(size_t)min(gi, e.ssq_groups - 1) * e.M + mc];
+    }
+  } else if constexpr (needs_norm(EPI)) {
+    float sum = 0.f;
+    if (nm < e.M) {
+#pragma unroll 4
+      for (int g = npt; g < e.ssq_groups; g += NP) sum += e.ssq[(size_t)g * e.M + nm];
+    }
+    norm_finish(sum);
   }
 
   // One batch: CHK k-blocks of weight fragments (HBM) and the matching
@@ -458,6 +474,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(GemmArgs g, EpiArgs e)
     Batch b;
     load_part(b, kb);
     compute(b);
+  }
+
+  if constexpr (NPRE > 0) {
+    // the norm sums loaded before the main loop, added in group order (the
+    // groups past NPRE * NP, above 4096 columns, loaded now)
+    float sum = 0.f;
+    if (nm < e.M) {
+#pragma unroll
+      for (int j = 0; j < NPRE; ++j)
+        if (npt + j * NP < e.ssq_groups) sum += npre[j];
+      for (int g = npt + NPRE * NP; g < e.ssq_groups; g += NP) sum += e.ssq[(size_t)g * e.M + nm];
+    }
+    norm_finish(sum);   // rnorm is read after the next barrier
   }
 
   // add the waves' sums in wave order, RB tiles per round
