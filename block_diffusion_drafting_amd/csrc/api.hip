@@ -220,7 +220,8 @@ struct PhaseTimer {
 
 dflash_status check_config(const dflash_config* c, bool target = false) {
   if (!c) return fail(DFLASH_E_ARG, "config is NULL");
-  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "bad dtype %d", (int)c->dtype);
+  const int32_t dt = abi_int(c->dtype);
+  if (dt != DFLASH_F32 && dt != DFLASH_BF16) return fail(DFLASH_E_ARG, "bad dtype %d", dt);
   if (c->hidden <= 0 || c->hidden % 64) return fail(DFLASH_E_SHAPE, "hidden %d must be a positive multiple of 64", c->hidden);
   if (c->n_layers < 0 || c->n_layers > 256) return fail(DFLASH_E_SHAPE, "n_layers %d out of range", c->n_layers);
   if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_E_SHAPE, "head_dim %d: 64 or 128 supported", c->head_dim);
@@ -1349,12 +1350,13 @@ dflash_status dflash_decay_ce(const void* logits, dflash_dtype dtype, const int3
   if (!loss || !workspace) return fail(DFLASH_E_ARG, "NULL pointer");
   if (rows > 0 && (!logits || !targets || !ce)) return fail(DFLASH_E_ARG, "NULL pointer");
   if ((uintptr_t)workspace % 8) return fail(DFLASH_E_ARG, "workspace not 8-byte aligned");
-  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return fail(DFLASH_E_ARG, "dtype = %d", (int)dtype);
+  const int32_t dt = abi_int(dtype);
+  if (dt != DFLASH_F32 && dt != DFLASH_BF16) return fail(DFLASH_E_ARG, "dtype = %d", dt);
   if (rows < 0) return fail(DFLASH_E_ARG, "rows = %d", rows);
   if (vocab < 1) return fail(DFLASH_E_ARG, "vocab = %d", vocab);
   if (block < 1) return fail(DFLASH_E_ARG, "block = %d", block);
   if (!(gamma > 0.0) || !std::isfinite(gamma)) return fail(DFLASH_E_ARG, "gamma = %g", gamma);
-  HIP_TRY(launch_decay_ce(logits, (int)dtype, targets, rows, vocab, block, gamma, loss, ce, rows > 0 ? grad : nullptr,
+  HIP_TRY(launch_decay_ce(logits, dt, targets, rows, vocab, block, gamma, loss, ce, rows > 0 ? grad : nullptr,
                           (double*)workspace, (hipStream_t)stream));
   return DFLASH_OK;
 }

@@ -23,6 +23,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// The int32 a caller stored in an enum field or parameter of the C ABI.  C
+// lets such an enum hold any int, while loading a value outside its
+// enumerators through the C++ enum type is undefined, so the bytes are read.
+template <typename E>
+inline int32_t abi_int(const E& v) {
+  static_assert(sizeof(E) == sizeof(int32_t), "C ABI enums are 32-bit");
+  int32_t i;
+  __builtin_memcpy(&i, &v, sizeof i);
+  return i;
+}
+
 constexpr int WAVE = 64;
 constexpr int FRAG_BYTES = 16;
 constexpr int BLOCK_BYTES = WAVE * FRAG_BYTES;  // one 16-row x 64-byte tile block

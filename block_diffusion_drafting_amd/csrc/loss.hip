@@ -488,7 +488,8 @@ extern "C" dflash_status dflash_decay_ce_noalloc(const void* logits, dflash_dtyp
   using namespace dflash;
   if (!loss) return dflash_set_error(DFLASH_E_ARG, "NULL pointer");
   if (rows > 0 && (!logits || !targets || !ce)) return dflash_set_error(DFLASH_E_ARG, "NULL pointer");
-  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return dflash_set_error(DFLASH_E_ARG, "bad dtype");
+  const int32_t dt = abi_int(dtype);
+  if (dt != DFLASH_F32 && dt != DFLASH_BF16) return dflash_set_error(DFLASH_E_ARG, "bad dtype");
   if (rows < 0) return dflash_set_error(DFLASH_E_ARG, "rows < 0");
   if (vocab < 1) return dflash_set_error(DFLASH_E_ARG, "vocab < 1");
   if (block < 1) return dflash_set_error(DFLASH_E_ARG, "block < 1");
@@ -512,7 +513,7 @@ extern "C" dflash_status dflash_decay_ce_noalloc(const void* logits, dflash_dtyp
     }
     ptr = g_scratch_dev[dev];
   }
-  const hipError_t e = launch_decay_ce(logits, (int)dtype, targets, rows, vocab, block, gamma, loss, ce,
+  const hipError_t e = launch_decay_ce(logits, dt, targets, rows, vocab, block, gamma, loss, ce,
                                        rows > 0 ? grad : nullptr, (double*)ptr, (hipStream_t)stream);
   if (e != hipSuccess) return dflash_set_error(DFLASH_E_HIP, hipGetErrorString(e));
   return DFLASH_OK;
