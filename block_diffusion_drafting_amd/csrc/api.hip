@@ -139,9 +139,13 @@ struct dflash_ctx {
   Buf fixcnt;   // arrival counters of split-K products (zero between launches)
   Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
   // L2 warm-up of the output projection's weights by spare blocks of the
-  // attention kernel (fragments per product wave; measured on the
-  // Qwen3-4B-shaped K = 16 step: its whole weight set pays)
-  int warm_o = 16;
+  // attention kernel, and of the gate/up projection's by spare blocks of
+  // the attention combine (fragments per product wave).  Measured on the
+  // Qwen3-4B-shaped K = 16 block: the output projection's whole weight set
+  // pays (0.4865 -> 0.4813 ms); gate/up's does not (16 fragments: gate/up
+  // 110 -> 98 us per block, the combine 44 -> 54 us, the block 0.4745 ->
+  // 0.4788 ms), so it is off by default.
+  int warm_o = 16, warm_gu = 0;
   // attention grid: 8-wave workgroup equivalents per compute unit, and the
   // shortest key split (a multiple of 64)
   int attn_wgs_per_cu = 2;
@@ -513,6 +517,7 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
   c->seq.assign(batch, DevSeq{});
   c->pst.enabled = env_int("DFLASH_PERSISTENT", 0, 0, 1) != 0;
   c->warm_o = env_int("DFLASH_WARM_O", c->warm_o, 0, 64);
+  c->warm_gu = env_int("DFLASH_WARM_GU", c->warm_gu, 0, 64);
   c->attn_wgs_per_cu = env_int("DFLASH_ATTN_WGS_PER_CU", c->attn_wgs_per_cu, 1, 16);
   c->attn_min_split = round_up(env_int("DFLASH_ATTN_MIN_SPLIT", c->attn_min_split, 64, 1 << 20), 64);
   c->attn_stream_mb = env_int("DFLASH_ATTN_STREAM_MB", c->attn_stream_mb, 0, 1 << 20);
@@ -1080,7 +1085,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
     }
     {
       PhaseTimer tm(c, PH_COMBINE, s);
-      HIP_TRY((launch_attn_combine<CT, T>(a, of, s)));
+      HIP_TRY((launch_attn_combine<CT, T>(a, of, s, make_warm<T>(EPI_SWIGLU, m->gu[l], M, c->warm_gu))));
     }
     // The output projection and the down projection add into the residual
     // and write the next norm's inputs (x * gain in frag layout, sums of

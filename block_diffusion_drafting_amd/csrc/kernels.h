@@ -237,7 +237,7 @@ template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Merge attention splits in index order; write o (frag layout over nq*d).
 template <typename CT, typename T>
-hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s, const Warm& warm = Warm{});
 
 // x[m] = E[id], xg = x * gain -> frag, ssq per 64-column group; keys = 0.
 template <typename T>
