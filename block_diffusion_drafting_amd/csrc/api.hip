@@ -139,13 +139,10 @@ struct dflash_ctx {
   Buf fixcnt;   // arrival counters of split-K products (zero between launches)
   Buf xg_hi, xg_lo, o_hi, o_lo, act_hi, act_lo, c_hi, c_lo;   // frag-layout activations
   // L2 warm-up of the output projection's weights by spare blocks of the
-  // attention kernel, and of the gate/up projection's by spare blocks of
-  // the attention combine (fragments per product wave).  Measured on the
-  // Qwen3-4B-shaped K = 16 block: the output projection's whole weight set
-  // pays (0.4865 -> 0.4813 ms); gate/up's does not (16 fragments: gate/up
-  // 110 -> 98 us per block, the combine 44 -> 54 us, the block 0.4745 ->
-  // 0.4788 ms), so it is off by default.
-  int warm_o = 16, warm_gu = 0;
+  // attention kernel (fragments per product wave; measured on the
+  // Qwen3-4B-shaped K = 16 block: its whole weight set pays, 0.4865 ->
+  // 0.4813 ms)
+  int warm_o = 16;
   // attention grid: 8-wave workgroup equivalents per compute unit, and the
   // shortest key split (a multiple of 64)
   int attn_wgs_per_cu = 2;
@@ -517,7 +514,6 @@ dflash_status dflash_ctx_create(const dflash_model* m, int32_t batch, const int3
   c->seq.assign(batch, DevSeq{});
   c->pst.enabled = env_int("DFLASH_PERSISTENT", 0, 0, 1) != 0;
   c->warm_o = env_int("DFLASH_WARM_O", c->warm_o, 0, 64);
-  c->warm_gu = env_int("DFLASH_WARM_GU", c->warm_gu, 0, 64);
   c->attn_wgs_per_cu = env_int("DFLASH_ATTN_WGS_PER_CU", c->attn_wgs_per_cu, 1, 16);
   c->attn_min_split = round_up(env_int("DFLASH_ATTN_MIN_SPLIT", c->attn_min_split, 64, 1 << 20), 64);
   c->attn_stream_mb = env_int("DFLASH_ATTN_STREAM_MB", c->attn_stream_mb, 0, 1 << 20);
@@ -943,6 +939,7 @@ struct FusedCtx {
   int n_ctx = 0;
   int mt0 = 0;
   Frag x{};
+  bool embedded = false;   // the block rows were embedded with the context rows' finalize
 };
 
 // Block verification by a target model: the same layer sequence, causal,
@@ -1008,7 +1005,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
   if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d) * sizeof(float))))
     return st;
 
-  {
+  if (!fused.embedded) {
     PhaseTimer tm(c, PH_EMBED, s);
     HIP_TRY(launch_embed<T>(ids, m->embed, L > 0 ? m->attn_gain(0) : m->final_gain(), M, H, cf.vocab,
                             (float*)c->x.p, xg, (float*)c->ssq.p, (unsigned long long*)c->keys.p, s));
@@ -1085,7 +1082,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
     }
     {
       PhaseTimer tm(c, PH_COMBINE, s);
-      HIP_TRY((launch_attn_combine<CT, T>(a, of, s, make_warm<T>(EPI_SWIGLU, m->gu[l], M, c->warm_gu))));
+      HIP_TRY((launch_attn_combine<CT, T>(a, of, s)));
     }
     // The output projection and the down projection add into the residual
     // and write the next norm's inputs (x * gain in frag layout, sums of
@@ -1175,15 +1172,25 @@ static dflash_status step_impl(dflash_ctx* c, const void* feats, const int32_t* 
   if ((st = ensure(c->alloc, c->rowmap, sizeof(RowMap) * total)) ||
       (st = ensure_frag(c, c->xg_hi, c->xg_lo, sizeof(T) == 2, mt_all, H * m->es / 64, s, fused.x)))
     return st;
+  // the block rows' residual, norm sums and argmax keys, sized as
+  // draft_impl sizes them (which then finds them in place)
+  const int Mb = B * K;
+  if ((st = ensure(c->alloc, c->x, (size_t)Mb * H * 4)) || (st = ensure(c->alloc, c->ssq, (size_t)(H / 16) * Mb * 4)) ||
+      (st = ensure(c->alloc, c->keys, (size_t)Mb * 8)))
+    return st;
   EpiArgs e = base_epi(c, total);
   const Frag none{};
   GemmPlan p;
   if ((st = run_gemm<T>(c, PH_FC, EPI_PART, m->fc, none, feats, m->cfg.n_feat * H, total, e, s, &p))) return st;
   {
+    // the context rows' finalize and the block rows' embedding, one launch
     PhaseTimer tm(c, PH_FCFIN, s);
-    HIP_TRY(launch_fc_finalize<T>((const float*)c->part.p, p.nsplit, mtc, total, H, ri, B, nullptr,
-                                  (RowMap*)c->rowmap.p, c->seq_dev, fused.x, mtb * 16, s));
+    HIP_TRY(launch_fc_finalize_embed<T>((const float*)c->part.p, p.nsplit, mtc, total, H, ri, B,
+                                        (RowMap*)c->rowmap.p, c->seq_dev, fused.x, mtb * 16, ids, m->embed,
+                                        m->attn_gain(0), Mb, m->cfg.vocab, (float*)c->x.p, fused.x,
+                                        (float*)c->ssq.p, (unsigned long long*)c->keys.p, s));
   }
+  fused.embedded = true;
   for (int b = 0; b < B; ++b) c->seq[b].ctx_len += n_new[b];
   return draft_impl<T>(c, ids, K, draft, logits, hidden, s, fused);
 }

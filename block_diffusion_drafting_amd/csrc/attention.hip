@@ -692,20 +692,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 // (frag layout of the model type T over nq*d, input of the output
 // projection).
 template <typename T, int D, int Q>
-__global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag out, Warm warm) {
+__global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag out) {
   constexpr int NDT = D / 16;
   constexpr int BATCH = 8;
   __shared__ float sm[Q][4][64], sl[Q][4][64];
-  __shared__ __attribute__((aligned(1024))) f32x4 so[Q][4][64];
+  __shared__ f32x4 so[Q][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // appended workgroups warm the gate/up projection's weights instead (one
-  // KiB of `so` per wave); the blocks that pad the grid to a multiple of 8
-  // before them do nothing
-  if (warm.w && (int)blockIdx.x >= warm.first) {
-    warm_consumer(warm, (int)blockIdx.x - warm.first, 4 * Q, wave, lane, (lds_void_t*)((uint8_t*)so + wave * 1024));
-    return;
-  }
-  if ((int)blockIdx.x >= a.B * a.nkv * a.qgroups * NDT) return;
   const int qt = wave & 3, quarter = wave >> 2;
   const int g4 = lane >> 4, col = lane & 15;
   int u = blockIdx.x;
@@ -831,26 +823,19 @@ template hipError_t launch_attention<f16_t>(const AttnArgs&, hipStream_t);
 template hipError_t launch_attention<float>(const AttnArgs&, hipStream_t);
 
 template <typename CT, typename T>
-hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s, const Warm& warm_in) {
-  unsigned nblk = (unsigned)a.B * a.nkv * a.qgroups * (a.d / 16);
-  Warm warm = warm_in;
-  if (warm.w) {
-    nblk = (nblk + 7u) / 8u * 8u;
-    warm.first = (int)nblk;
-    nblk += (unsigned)warm.consumers;
-  }
-  dim3 grid(nblk);
+hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s) {
+  dim3 grid((unsigned)a.B * a.nkv * a.qgroups * (a.d / 16));
   const bool few = a.max_splits <= 8;   // one part: four waves per workgroup
   switch (a.d * 2 + (few ? 1 : 0)) {
-    case 64 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 4>), grid, dim3(1024), 0, s, a, o, warm); break;
-    case 64 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 1>), grid, dim3(256), 0, s, a, o, warm); break;
-    case 128 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4>), grid, dim3(1024), 0, s, a, o, warm); break;
-    case 128 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1>), grid, dim3(256), 0, s, a, o, warm); break;
+    case 64 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 4>), grid, dim3(1024), 0, s, a, o); break;
+    case 64 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 1>), grid, dim3(256), 0, s, a, o); break;
+    case 128 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4>), grid, dim3(1024), 0, s, a, o); break;
+    case 128 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1>), grid, dim3(256), 0, s, a, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-template hipError_t launch_attn_combine<f16_t, bf16_t>(const AttnArgs&, Frag, hipStream_t, const Warm&);
-template hipError_t launch_attn_combine<float, float>(const AttnArgs&, Frag, hipStream_t, const Warm&);
+template hipError_t launch_attn_combine<f16_t, bf16_t>(const AttnArgs&, Frag, hipStream_t);
+template hipError_t launch_attn_combine<float, float>(const AttnArgs&, Frag, hipStream_t);
 
 }  // namespace dflash

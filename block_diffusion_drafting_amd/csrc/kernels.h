@@ -237,14 +237,13 @@ template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Merge attention splits in index order; write o (frag layout over nq*d).
 template <typename CT, typename T>
-hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s, const Warm& warm = Warm{});
+hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s);
 
 // x[m] = E[id], xg = x * gain -> frag, ssq per 64-column group; keys = 0.
 template <typename T>
 hipError_t launch_embed(const int32_t* ids, const void* embed, const float* gain, int M, int H,
                         int V, float* x, Frag xg, float* ssq, unsigned long long* keys,
                         hipStream_t s);
-// x += sum of split-K partials (fixed order); xg = x * gain -> frag; ssq.
 // Rows of one context append: rows [start[b], start[b+1]) belong to
 // sequence b and go to slots ctx0[b] + (row - start[b]) (host values).
 struct RowInfo {
@@ -258,11 +257,21 @@ template <typename T>
 hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri, int B,
                               const int32_t* positions, RowMap* rowmap, DevSeq* seqs, Frag cbuf,
                               int row0, hipStream_t s);
-// out[m][tap*H + h] = x[m][h] in the model type (a tapped hidden state;
-// out rows are n_taps*H long).
+// launch_fc_finalize (without positions) and launch_embed as one launch
+// (the fused step: the appended context rows and the block rows of the
+// first QKV product's activations are independent)
+template <typename T>
+hipError_t launch_fc_finalize_embed(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri,
+                                    int B, RowMap* rowmap, DevSeq* seqs, Frag cbuf, int row0,
+                                    const int32_t* ids, const void* embed, const float* gain, int Mb, int V,
+                                    float* x, Frag xg, float* ssq, unsigned long long* keys, hipStream_t s);
+// x += sum of split-K partials (fixed order); xg = x * gain -> frag; ssq
+// per 64-column group.
 template <typename T>
 hipError_t launch_resid_norm(const float* part, int nsplit, int mtiles, int M, int H, float* x,
                              const float* gain, Frag xg, float* ssq, hipStream_t s);
+// out[m][tap*H + h] = x[m][h] in the model type (a tapped hidden state;
+// out rows are n_taps*H long).
 template <typename T>
 hipError_t launch_tap(const float* x, int M, int H, int tap, int n_taps, void* out, hipStream_t s);
 // draft ids from argmax keys; optional final-normed hidden rows.

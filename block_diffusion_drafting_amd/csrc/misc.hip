@@ -11,13 +11,28 @@ namespace dflash {
 // 64c..64c+63, keys[m] = 0 (argmax of this block).
 // Thread t: row (t / 16) of the tile, columns 4*(t % 16) .. +3 of the slab.
 // ---------------------------------------------------------------------------
+struct EmbedArgs {
+  const int32_t* ids;
+  const void* embed;
+  const float* gain;
+  int M, H, V;
+  float* x;
+  Frag xg;
+  float* ssq;
+  unsigned long long* keys;
+};
+
+// Block (bx, by) of the embedding: rows 16 bx.., columns 64 by..
 template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const int32_t* ids, const T* embed,
-                                                    const float* gain, int M, int H, int V,
-                                                    float* x, Frag xg, float* ssq,
-                                                    unsigned long long* keys) {
-  const int m = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int n0 = blockIdx.y * 64 + (threadIdx.x & 15) * 4;
+__device__ __forceinline__ void embed_block(const EmbedArgs& a, int bx, int by) {
+  const int32_t* ids = a.ids;
+  const T* embed = (const T*)a.embed;
+  const float* gain = a.gain;
+  const int M = a.M, H = a.H, V = a.V;
+  float* x = a.x;
+  const Frag& xg = a.xg;
+  const int m = bx * 16 + (threadIdx.x >> 4);
+  const int n0 = by * 64 + (threadIdx.x & 15) * 4;
   float ss = 0.f;
   if (m < M) {
     int id = ids[m];
@@ -36,9 +51,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* ids, const T*
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   if (m < M && (threadIdx.x & 15) == 0) {
-    ssq[(size_t)blockIdx.y * M + m] = ss;
-    if (blockIdx.y == 0) keys[m] = 0ull;
+    a.ssq[(size_t)by * M + m] = ss;
+    if (by == 0) a.keys[m] = 0ull;
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+  embed_block<T>(a, blockIdx.x, blockIdx.y);
 }
 
 template <typename T>
@@ -46,8 +66,8 @@ hipError_t launch_embed(const int32_t* ids, const void* embed, const float* gain
                         int V, float* x, Frag xg, float* ssq, unsigned long long* keys,
                         hipStream_t s) {
   dim3 grid((M + 15) / 16, H / 64);
-  hipLaunchKernelGGL((embed_kernel<T>), grid, dim3(256), 0, s, ids, (const T*)embed, gain, M, H,
-                     V, x, xg, ssq, keys);
+  const EmbedArgs a{ids, embed, gain, M, H, V, x, xg, ssq, keys};
+  hipLaunchKernelGGL((embed_kernel<T>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template hipError_t launch_embed<bf16_t>(const int32_t*, const void*, const float*, int, int, int,
@@ -146,22 +166,38 @@ __device__ __forceinline__ RowMap map_row(const RowInfo& ri, int B, int j, const
   return r;
 }
 
+struct FcFinArgs {
+  const float* part;
+  int nsplit, mtiles, M, H;
+  RowInfo ri;
+  int B;
+  const int32_t* positions;
+  RowMap* rowmap;
+  DevSeq* seqs;
+  Frag cbuf;
+  int row0;
+};
+
+// Block (bx, by): rows 16 bx.., columns 64 by..
 template <typename T>
-__global__ __launch_bounds__(256) void fc_finalize_kernel(const float* part, int nsplit, int mtiles,
-                                                          int M, int H, RowInfo ri, int B,
-                                                          const int32_t* positions, RowMap* rowmap,
-                                                          DevSeq* seqs, Frag cbuf, int row0) {
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int b = threadIdx.x; b < B; b += blockDim.x) seqs[b].ctx_len = ri.ctx0[b] + ri.start[b + 1] - ri.start[b];
-  const int m = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int n0 = blockIdx.y * 64 + (threadIdx.x & 15) * 4;
+__device__ __forceinline__ void fc_finalize_block(const FcFinArgs& a, int bx, int by) {
+  const int B = a.B, M = a.M, H = a.H;
+  if (bx == 0 && by == 0)
+    for (int b = threadIdx.x; b < B; b += blockDim.x) a.seqs[b].ctx_len = a.ri.ctx0[b] + a.ri.start[b + 1] - a.ri.start[b];
+  const int m = bx * 16 + (threadIdx.x >> 4);
+  const int n0 = by * 64 + (threadIdx.x & 15) * 4;
   if (m >= M) return;
-  const RowMap rm = map_row(ri, B, m, positions);
-  if (blockIdx.y == 0 && (threadIdx.x & 15) == 0) rowmap[m] = rm;
-  const f32x4 c = sum_parts(part, nsplit, H / 16, mtiles, m, n0);
-  *gp((f32x4*)((float*)seqs[rm.b].ctxbuf + (size_t)rm.slot * H + n0)) = c;
+  const RowMap rm = map_row(a.ri, B, m, a.positions);
+  if (by == 0 && (threadIdx.x & 15) == 0) a.rowmap[m] = rm;
+  const f32x4 c = sum_parts(a.part, a.nsplit, H / 16, a.mtiles, m, n0);
+  *gp((f32x4*)((float*)a.seqs[rm.b].ctxbuf + (size_t)rm.slot * H + n0)) = c;
   float v[4] = {c[0], c[1], c[2], c[3]};
-  frag_store<T, 4>(cbuf, row0 + m, n0, v);
+  frag_store<T, 4>(a.cbuf, a.row0 + m, n0, v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fc_finalize_kernel(FcFinArgs a) {
+  fc_finalize_block<T>(a, blockIdx.x, blockIdx.y);
 }
 
 template <typename T>
@@ -170,10 +206,43 @@ hipError_t launch_fc_finalize(const float* part, int nsplit, int mtiles, int M, 
                               int row0, hipStream_t s) {
   if (B > DFLASH_ROWMAP_MAX) return hipErrorInvalidValue;
   dim3 grid((M + 15) / 16, H / 64);
-  hipLaunchKernelGGL((fc_finalize_kernel<T>), grid, dim3(256), 0, s, part, nsplit, mtiles, M, H, ri, B,
-                     positions, rowmap, seqs, cbuf, row0);
+  const FcFinArgs a{part, nsplit, mtiles, M, H, ri, B, positions, rowmap, seqs, cbuf, row0};
+  hipLaunchKernelGGL((fc_finalize_kernel<T>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+// Blocks [0, nf): the context rows (fc_finalize_block), then the block
+// rows' embedding (embed_block); both grids are m-tile major.
+template <typename T>
+__global__ __launch_bounds__(256) void fc_finalize_embed_kernel(FcFinArgs f, EmbedArgs e) {
+  const int fx = (f.M + 15) / 16, nf = fx * (f.H / 64);
+  const int b = blockIdx.x;
+  if (b < nf) {
+    fc_finalize_block<T>(f, b % fx, b / fx);
+  } else {
+    const int ex = (e.M + 15) / 16, k = b - nf;
+    embed_block<T>(e, k % ex, k / ex);
+  }
+}
+
+template <typename T>
+hipError_t launch_fc_finalize_embed(const float* part, int nsplit, int mtiles, int M, int H, const RowInfo& ri,
+                                    int B, RowMap* rowmap, DevSeq* seqs, Frag cbuf, int row0,
+                                    const int32_t* ids, const void* embed, const float* gain, int Mb, int V,
+                                    float* x, Frag xg, float* ssq, unsigned long long* keys, hipStream_t s) {
+  if (B > DFLASH_ROWMAP_MAX || M < 1 || Mb < 1) return hipErrorInvalidValue;
+  const FcFinArgs f{part, nsplit, mtiles, M, H, ri, B, nullptr, rowmap, seqs, cbuf, row0};
+  const EmbedArgs e{ids, embed, gain, Mb, H, V, x, xg, ssq, keys};
+  const unsigned nblk = (unsigned)(((M + 15) / 16) * (H / 64) + ((Mb + 15) / 16) * (H / 64));
+  hipLaunchKernelGGL((fc_finalize_embed_kernel<T>), dim3(nblk), dim3(256), 0, s, f, e);
+  return hipGetLastError();
+}
+template hipError_t launch_fc_finalize_embed<bf16_t>(const float*, int, int, int, int, const RowInfo&, int, RowMap*,
+                                                     DevSeq*, Frag, int, const int32_t*, const void*, const float*,
+                                                     int, int, float*, Frag, float*, unsigned long long*, hipStream_t);
+template hipError_t launch_fc_finalize_embed<float>(const float*, int, int, int, int, const RowInfo&, int, RowMap*,
+                                                    DevSeq*, Frag, int, const int32_t*, const void*, const float*,
+                                                    int, int, float*, Frag, float*, unsigned long long*, hipStream_t);
 template hipError_t launch_fc_finalize<bf16_t>(const float*, int, int, int, int, const RowInfo&, int,
                                                const int32_t*, RowMap*, DevSeq*, Frag, int, hipStream_t);
 template hipError_t launch_fc_finalize<float>(const float*, int, int, int, int, const RowInfo&, int,

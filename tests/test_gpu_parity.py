@@ -111,16 +111,13 @@ def test_small_bf16_long_splits_poisoned(monkeypatch, K, stream):
     assert np.all(np.isfinite(g["logits"]))
 
 
-@pytest.mark.parametrize("warm", [("16", "16"), ("0", "0")])
+@pytest.mark.parametrize("warm", ["16", "0"])
 def test_small_bf16_l2_warm_up_settings(monkeypatch, warm):
-    """The L2 warm-up workgroups appended to the attention kernel (for the
-    output projection) and to the attention combine (for gate/up) load
-    weights and discard them: outputs match the oracle with them on and
-    off."""
-    o, gu = warm
-    say(f"case: warm-up O={o} GU={gu}")
-    monkeypatch.setenv("DFLASH_WARM_O", o)
-    monkeypatch.setenv("DFLASH_WARM_GU", gu)
+    """The L2 warm-up workgroups appended to the attention kernel for the
+    output projection load weights and discard them: outputs match the
+    oracle with them on and off."""
+    say(f"case: warm-up O={warm}")
+    monkeypatch.setenv("DFLASH_WARM_O", warm)
     p = Pair(SMALL, 43, 2, gain_std=0.1)
     _prefill(p, [200, 77])
     p.compare(_ids(44, 2, 16, SMALL.vocab))
