@@ -16,8 +16,9 @@ RoPE against complex multiplication, single-key and uniform-attention special
 cases, context-permutation, global position-shift, block-permutation and
 batch invariances, GQA == MHA with duplicated KV weights, incremental ==
 one-shot projection, exhaustive acceptance enumeration, the closed form of
-the expected acceptance length under independent agreement, and the growth
-and state-advance invariants.
+the expected acceptance length under independent agreement, the growth
+and state-advance invariants, and the bf16 decode and round-to-nearest-even
+against their definitions (hand bit patterns, every finite pattern).
 
 Parity unpinned: whether this reading of the pages matches the exact
 architecture of the trained DFlash drafters (placement of norms, the
