@@ -307,7 +307,7 @@ def spread(ms):
             "p90": round(float(np.percentile(ms, 90)), 4), "mean": round(float(ms.mean()), 4), "n": int(ms.size)}
 
 
-def north_star_extras(args, torch, dfl, wl, model, ctx, K, ids0, lens0, mb):
+def headline_extras(args, torch, dfl, wl, model, ctx, K, ids0, lens0, mb):
     """The figures the goal names beside the headline step: draft-block
     latency warm and cold (median / p10 / p90), MFMA utilisation, the
     draft latency at K = 16 and K = 128 over a 4096-position context (the
@@ -962,7 +962,7 @@ def main():
                          "launches": dom_n, "bytes_per_launch": int(dom_bytes)},
         }
         if not args.no_extras and args.workload == 1 and not args.K:
-            out.update(north_star_extras(args, torch, dfl, wl, model, ctx, K, dev[0][0], lens0, mb))
+            out.update(headline_extras(args, torch, dfl, wl, model, ctx, K, dev[0][0], lens0, mb))
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(wl, K, w, args.cpu_steps)
         results.append(out)
