@@ -514,9 +514,9 @@ __device__ __forceinline__ void loader(const PArgs& a, PShared& sh, l_u32x4* rin
             if ((int)(written + n - free_upto) <= 0) break;
             if (!loader_keep_waiting(a, sh, t0, cnt, lane)) {
               // abandoned: drop the rest of the stream and publish nothing
-              // more; the loop ends with this round of loads.  (Leaving the
-              // loop from here would add an edge into it that shortens the
-              // waits of all its loads.)
+              // more; the loop ends after this pass over the register sets.
+              // (Leaving the loop from here would add an edge into it that
+              // shortens the waits of all its loads.)
               done = true;
               live = false;
               written = issued;
