@@ -37,6 +37,23 @@
 
 namespace dflash {
 
+// Workgroup barrier that leaves vector-memory loads in flight.
+// __syncthreads() also fences at workgroup scope, and its release completes
+// every outstanding vector-memory load, the prefetches of later chunks
+// included, which shortens a multi-chunk pipeline to one chunk in flight
+// across each barrier.  The attention pipelines only need their LDS traffic
+// ordered: this wave's LDS reads and writes are completed (lgkmcnt(0)), the
+// stage to be read after the barrier is covered by the explicit vmcnt wait
+// (direct loads) or the compiler's wait before the LDS store (register
+// staging) that precede the call, and the compiler-only fences keep memory
+// accesses on their side of the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Keys per LDS chunk (two chunks are resident): 64, or 32 for fp32 operands
 // with head_dim 128.
 template <typename T, int D>
@@ -345,11 +362,11 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
     gload(r0, cbeg(c + 2));
     compute(cbeg(c), cfin(c), 0);
     lstore(r1, 1, cbeg(c + 1), cfin(c + 1));
-    __syncthreads();
+    lds_barrier();
     gload(r1, cbeg(c + 3));
     compute(cbeg(c + 1), cfin(c + 1), 1);
     lstore(r0, 0, cbeg(c + 2), cfin(c + 2));
-    __syncthreads();
+    lds_barrier();
   }
   // The last one to three chunks: c in buffer 0, c+1 (if any) in r1.
   if (c + 2 < nchunks) gload(r0, cbeg(c + 2));
@@ -414,13 +431,10 @@ __device__ __forceinline__ void wait_vm() {
 
 // One 16-byte-per-lane direct load to LDS (global_load_lds_dwordx4): lane
 // l's 16 bytes at base + off go to LDS address lds + 16 l; lds must be the
-// same in every lane.  Through the compiler's builtin, so the compiler
-// counts these loads: it completes all of them before each workgroup
-// barrier (a barrier orders LDS writes), which leaves one chunk in flight
-// across a barrier instead of three.  Measured on the Qwen3-4B K sweep
-// against loads issued from inline assembly: attention +1 to +15 % (K = 1024
-// / 64), the whole draft block +0.2 to +0.7 %.  The waits below remain as
-// the pipeline's own statement of what each step needs.
+// same in every lane.  A load decrements the vector-memory count once its
+// bytes are in LDS, so the explicit vmcnt waits below, taken before a
+// barrier (lds_barrier, which leaves later chunks' loads in flight), make a
+// stage visible to every wave.
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_t*)lds, 16, 0, 0);
 }
@@ -662,7 +676,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
     else if (later == 2) wait_vm<2 * LPW * 2>();
     else if (later == 1) wait_vm<2 * LPW>();
     else wait_vm<0>();
-    __syncthreads();
+    lds_barrier();
     if (c + NS - 1 < nchunks) issue(c + NS - 1);
     compute(c);
   }
