@@ -644,7 +644,8 @@ static Warm make_warm(int epi, const Packed& W, int M, int frags, bool force_spl
   if (frags <= 0) return w;
   GemmPlan p = plan_gemm(epi, W, M, sizeof(T) == 2, false);
   (void)force_split;   // the hi/lo choice does not change which weights a workgroup reads
-  if (uses_head_kernel(epi, p, W.n_tiles, (int)sizeof(T))) return w;   // another tile-to-workgroup map: not warmed
+  // another tile-to-workgroup map: not warmed
+  if (p.wide || uses_head_kernel(epi, p, W.n_tiles, (int)sizeof(T))) return w;
   w.w = W.w;
   w.nkb = W.nkb;
   w.n_tiles = W.n_tiles;

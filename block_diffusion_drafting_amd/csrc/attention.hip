@@ -37,23 +37,6 @@
 
 namespace dflash {
 
-// Workgroup barrier that leaves vector-memory loads in flight.
-// __syncthreads() also fences at workgroup scope, and its release completes
-// every outstanding vector-memory load, the prefetches of later chunks
-// included, which shortens a multi-chunk pipeline to one chunk in flight
-// across each barrier.  The attention pipelines only need their LDS traffic
-// ordered: this wave's LDS reads and writes are completed (lgkmcnt(0)), the
-// stage to be read after the barrier is covered by the explicit vmcnt wait
-// (direct loads) or the compiler's wait before the LDS store (register
-// staging) that precede the call, and the compiler-only fences keep memory
-// accesses on their side of the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Keys per LDS chunk (two chunks are resident): 64, or 32 for fp32 operands
 // with head_dim 128.
 template <typename T, int D>
@@ -421,23 +404,6 @@ constexpr int MQ_STAGES = 4;
 
 __device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
 __device__ __forceinline__ int vswz(int t) { return (t >> 1) & 7; }
-
-// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima = no wait).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One 16-byte-per-lane direct load to LDS (global_load_lds_dwordx4): lane
-// l's 16 bytes at base + off go to LDS address lds + 16 l; lds must be the
-// same in every lane.  A load decrements the vector-memory count once its
-// bytes are in LDS, so the explicit vmcnt waits below, taken before a
-// barrier (lds_barrier, which leaves later chunks' loads in flight), make a
-// stage visible to every wave.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_t*)lds, 16, 0, 0);
-}
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void attention_mq_kernel(AttnArgs a) {
   using T = f16_t;

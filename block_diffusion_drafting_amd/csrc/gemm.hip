@@ -89,6 +89,29 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
     p.m_groups = (mtiles + 3) / 4;
   }
   const int T = W.n_tiles;
+  // One 128-row m-group with the hi/lo pair: the split-K product (EPI_PART,
+  // the output and down projections above four m-tiles) runs wide_kernel,
+  // eight tiles per workgroup (four per wave slot), with about one round of
+  // workgroups over its tile groups and splits of at least eight k-blocks.
+  // Measured at the Qwen3-4B shape, 128 rows, per launch: o + down average
+  // 21.1 -> 16.2 us (down 29 -> about 22 us with 12 splits); gate/up on
+  // wide_kernel was no faster than gemm_kernel in 64-row groups (46.2 vs
+  // 46.3 us), so it stays there.
+  if (p.split && mtiles > 4 && mtiles <= 8 && epi == EPI_PART && !rowmajor) {
+    p.wide = true;
+    p.mtt = 8;
+    p.m_groups = 1;
+    p.ntg = 4;
+    p.n_groups = (T + 2 * p.ntg - 1) / (2 * p.ntg);
+    int ns = kCUs / p.n_groups;
+    if (ns > W.nkb / 8) ns = W.nkb / 8;
+    if (ns < 1) ns = 1;
+    p.kbu = (W.nkb + ns - 1) / ns;
+    p.nsplit = (W.nkb + p.kbu - 1) / p.kbu;
+    p.part_floats = (size_t)p.nsplit * T * mtiles * 256;
+    p.fixed = false;
+    return p;
+  }
   if (is_part(epi)) {
     int ns = MAX_SPLITS;
     while (ns > 1 && W.nkb / ns < 8) ns /= 2;

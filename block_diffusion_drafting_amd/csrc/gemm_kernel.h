@@ -854,11 +854,182 @@ inline hipError_t launch_head(const GemmPlan& p, GemmArgs g, const EpiArgs& e, h
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Split-K products over one m-group of 128 rows with the hi/lo pair (bf16
+// model): the output and down projections above four m-tiles.  Four waves,
+// one workgroup per CU: wave w covers tile slot w % 2 (up to NTW tiles of
+// the workgroup's range) and m-half w / 2 (4 m-tiles), over the
+// workgroup's k-range.  Each k-block's activation fragments (8 m-tiles x
+// hi/lo) and weight fragments (the workgroup's tiles) are staged once per
+// workgroup in a ring of WIDE_STAGES LDS stages by direct loads, issued
+// WIDE_STAGES - 1 k-blocks ahead; each wave reads the next k-block's
+// fragments from LDS into its second register set while the MFMAs of the
+// current one run.  In gemm_kernel's form every wave loads its own 16
+// activation fragments per k-block through the vector-memory path with one
+// load batch in flight, which bounds the 128-row split products (measured
+// at the Qwen3-4B shape, 128 rows, per launch: o + down average 21.1 ->
+// 16.2 us).  Per k-block a CU reads 48 KiB from LDS and writes 24 KiB into
+// it beside 128 MFMAs per SIMD; a barrier and the direct loads add about
+// 170 and 180 cycles to the 740 of the LDS reads and MFMAs alone
+// (measured), which bounds this form near 1000 cycles per k-block.  The
+// epilogue is gemm_kernel's split-K store, per tile.
+// ---------------------------------------------------------------------------
+constexpr int WIDE_STAGES = 4;
+
+template <typename T, int NTW>
+__global__ __launch_bounds__(256, 1) void wide_kernel(GemmArgs g, EpiArgs e) {
+  static_assert(sizeof(T) == 2, "bf16 models (hi/lo pair)");
+  using E = Elem<T>;
+  constexpr int MT = 8, MPW = 4, XF = 2 * MT, FR = XF + 2 * NTW;
+  constexpr int DPW = (FR + 3) / 4;            // direct loads per wave per stage
+  constexpr int NF = 2 * MPW + NTW;            // fragments a wave reads per k-block
+  constexpr int NS = WIDE_STAGES;
+  constexpr int NW0 = DPW * (NS - 2), NW1 = DPW * (NS - 3);   // loads issued after the awaited stage
+  static_assert(NS >= 3 && NW0 < 64, "stages");
+  // One LDS object.  (With several, the compiler tells them apart and
+  // completes every outstanding direct load before each read of the ring;
+  // the explicit waits below are what order those reads.)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][4 * DPW][BLOCK_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ts = wave & 1, mp = wave >> 1;
+  // unit: tile group ng, split s
+  const int s = (int)blockIdx.x % g.nsplit, ng = (int)blockIdx.x / g.nsplit;
+  const int tile0 = (int)((long)ng * g.W.n_tiles / g.n_groups);
+  const int nt = (int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0;
+  const int wt0 = tile0 + (ts * nt) / 2;   // this wave's tiles: [wt0, wt0 + wnt), wnt <= NTW
+  const int wnt = __builtin_amdgcn_readfirstlane(tile0 + ((ts + 1) * nt) / 2 - wt0);
+  const int kbA = s * g.kbu;
+  const int nk = min(g.W.nkb, kbA + g.kbu) - kbA;   // >= 1: the plan leaves no split empty
+
+  // Direct load d of this wave fills stage fragment f = wave * DPW + d:
+  //   f < XF        activation part f / MT (hi, lo) of m-tile f % MT (an
+  //                 m-tile past the activation repeats its last one: those
+  //                 rows are never stored)
+  //   f < FR        weight tile (f - XF) % NTW of slot (f - XF) / NTW (a slot
+  //                 past its range repeats its last tile, never used)
+  //   otherwise     a repeat of fragment 0 into a spare slot, never read
+  // Offsets are 32-bit from the matrix base (checked at launch).
+  const uint8_t* dsrc[DPW];
+  uint32_t doff[DPW];
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int f = wave * DPW + d;
+    if (f < XF || f >= FR) {
+      const int fx = f < XF ? f : 0;
+      const int mt = min(fx % MT, g.X.mtiles - 1);
+      dsrc[d] = (const uint8_t*)(fx / MT ? g.X.lo : g.X.hi);
+      doff[d] = (uint32_t)(((size_t)mt * g.X.nkb + kbA) * BLOCK_BYTES + lane * FRAG_BYTES);
+    } else {
+      const int slot = (f - XF) / NTW, t = (f - XF) % NTW;
+      const int st0 = tile0 + (slot * nt) / 2, sn = tile0 + ((slot + 1) * nt) / 2 - st0;
+      const int tile = min(st0 + min(t, max(sn, 1) - 1), g.W.n_tiles - 1);
+      dsrc[d] = g.W.w;
+      doff[d] = (uint32_t)(((size_t)tile * g.W.nkb + kbA) * BLOCK_BYTES + lane * FRAG_BYTES);
+    }
+  }
+  // stage of k-block i of the range (past the end: its last k-block again)
+  auto issue = [&](int i) {
+    const uint32_t kb = (uint32_t)min(i, nk - 1) * BLOCK_BYTES;
+    uint8_t* st = &ring[i % NS][0][0];
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) dma16(dsrc[d], doff[d] + kb, st + (wave * DPW + d) * BLOCK_BYTES);
+  };
+  u32x4 fr[2][NF];
+  auto read = [&](u32x4 (&dst)[NF], int i) {
+    const uint8_t* st = &ring[i % NS][0][0] + lane * FRAG_BYTES;
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      dst[2 * m] = *(const u32x4*)(st + (mp * MPW + m) * BLOCK_BYTES);
+      dst[2 * m + 1] = *(const u32x4*)(st + (MT + mp * MPW + m) * BLOCK_BYTES);
+    }
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) dst[2 * MPW + t] = *(const u32x4*)(st + (XF + ts * NTW + t) * BLOCK_BYTES);
+  };
+  f32x4 acc[NTW][MPW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // hi then lo per k-block, k-blocks in order: the summation order of gemm_kernel's waves
+  auto compute = [&](const u32x4 (&f)[NF]) {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        acc[t][m] = E::mma(f[2 * MPW + t], f[2 * m], acc[t][m]);
+        acc[t][m] = E::mma(f[2 * MPW + t], f[2 * m + 1], acc[t][m]);
+      }
+  };
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p);
+  wait_vm<NW0>();
+  lds_barrier();
+  read(fr[0], 0);
+  // k-block i: wait for stage i + 1 and make it visible, refill the stage of
+  // k-block i - 1 (its reads completed before this barrier) with k-block
+  // i + NS - 1, read stage i + 1 into the other register set, and run k-block
+  // i's MFMAs on the set read one step earlier
+  auto step = [&](int i, int par, bool guard) {
+    wait_vm<NW1>();
+    lds_barrier();
+    issue(i + NS - 1);
+    read(fr[par ^ 1], i + 1);
+    if (!guard || i < nk) compute(fr[par]);
+  };
+  int i = 0;
+  for (; i + 2 <= nk; i += 2) {
+    step(i, 0, false);
+    step(i + 1, 1, false);
+  }
+  if (i < nk) step(i, 0, true);
+  wait_vm<0>();   // the stages issued past the end
+
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    if (t >= wnt) continue;   // uniform over the wave
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+      epilogue_tile<T, EPI_PART>(e, s, wt0 + t, mp * MPW + m, acc[t][m], lane, 1.f, nullptr);
+  }
+}
+
+template <typename T, int EPI>
+inline hipError_t launch_wide(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  if constexpr (sizeof(T) != 2 || EPI != EPI_PART) {
+    return hipErrorInvalidValue;
+  } else {
+    g.kbu = p.kbu;
+    g.nsplit = p.nsplit;
+    g.n_groups = p.n_groups;
+    g.m_groups = p.m_groups;
+    // one m-group; every tile in a range of at most 2 * ntg tiles (ntg per
+    // wave slot); direct-load offsets within 32 bits; every split non-empty
+    const size_t wbytes = (size_t)g.W.n_tiles * g.W.nkb * BLOCK_BYTES;
+    const size_t xbytes = (size_t)g.X.mtiles * g.X.nkb * BLOCK_BYTES;
+    if (!p.split || !g.X.lo || p.m_groups != 1 || g.X.mtiles < 1 || g.X.nkb < g.W.nkb || p.n_groups < 1 ||
+        (g.W.n_tiles + p.n_groups - 1) / p.n_groups > 2 * p.ntg || wbytes >= (1ull << 32) ||
+        xbytes >= (1ull << 32) || (size_t)(p.nsplit - 1) * p.kbu >= (size_t)g.W.nkb)
+      return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.n_groups * p.nsplit);
+    switch (p.ntg) {
+      case 2: hipLaunchKernelGGL((wide_kernel<T, 2>), grid, dim3(256), 0, s, g, e); break;
+      case 3: hipLaunchKernelGGL((wide_kernel<T, 3>), grid, dim3(256), 0, s, g, e); break;
+      case 4: hipLaunchKernelGGL((wide_kernel<T, 4>), grid, dim3(256), 0, s, g, e); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+}
+
 template <typename T, int EPI>
 hipError_t launch_gemm_epi(const GemmPlan& p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
   if constexpr ((EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) && sizeof(T) == 2) {
     if (uses_head_kernel(EPI, p, g.W.n_tiles, (int)sizeof(T))) return launch_head<T, EPI>(p, g, e, s);
   }
+  if (p.wide) return launch_wide<T, EPI>(p, g, e, s);
   g.kbu = p.kbu;
   g.nsplit = p.nsplit;
   g.n_groups = p.n_groups;

@@ -110,11 +110,12 @@ struct GemmArgs {
 
 struct GemmPlan {
   int mtt;     // m-tiles per group (1, 2, 4, 8)
-  int ntg;     // tiles per group
+  int ntg;     // tiles per group (wide_kernel: per wave slot, two slots per group)
   int kbu, nsplit, n_groups, m_groups;
   bool split;  // use hi + lo fragments
   bool rowmajor;
   bool fixed;  // fixed tile groups (the context path at prefill sizes)
+  bool wide;   // wide_kernel (128-row m-groups, activations and weights staged in LDS)
   size_t part_floats;
 };
 
@@ -174,6 +175,41 @@ struct Warm {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima = no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane direct load to LDS (global_load_lds_dwordx4): lane
+// l's 16 bytes at base + off go to LDS address lds + 16 l; lds must be the
+// same in every lane.  A load decrements the vector-memory count once its
+// bytes are in LDS, so an explicit vmcnt wait taken before a barrier
+// (lds_barrier, which leaves later stages' loads in flight) makes a stage
+// visible to every wave.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void_t*)lds, 16, 0, 0);
+}
+
+// Workgroup barrier that leaves vector-memory loads in flight.
+// __syncthreads() also fences at workgroup scope, and its release completes
+// every outstanding vector-memory load, the prefetches of later stages
+// included, which shortens a multi-stage pipeline to one stage in flight
+// across each barrier.  The staged pipelines only need their LDS traffic
+// ordered: this wave's LDS reads and writes are completed (lgkmcnt(0)), the
+// stage to be read after the barrier is covered by the explicit vmcnt wait
+// (direct loads) or the compiler's wait before the LDS store (register
+// staging) that precede the call, and the compiler-only fences keep memory
+// accesses on their side of the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Warm-up workgroup k with nw waves (this is wave `wave`): product
 // workgroup k's waves cw = wave, wave + nw, ... ; `slot` is this wave's own
