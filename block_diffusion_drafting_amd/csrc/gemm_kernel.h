@@ -855,7 +855,7 @@ inline hipError_t launch_head(const GemmPlan& p, GemmArgs g, const EpiArgs& e, h
 }
 
 // ---------------------------------------------------------------------------
-// Split-K products over one m-group of 128 rows with the hi/lo pair (bf16
+// Split-K products over m-groups of 128 rows with the hi/lo pair (bf16
 // model): the output and down projections above four m-tiles.  Four waves,
 // one workgroup per CU: wave w covers tile slot w % 2 (up to NTW tiles of
 // the workgroup's range) and m-half w / 2 (4 m-tiles), over the
@@ -894,8 +894,23 @@ __global__ __launch_bounds__(256, 1) void wide_kernel(GemmArgs g, EpiArgs e) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ts = wave & 1, mp = wave >> 1;
-  // unit: tile group ng, split s
-  const int s = (int)blockIdx.x % g.nsplit, ng = (int)blockIdx.x / g.nsplit;
+  // unit (tile group ng, split s) and m-group mg, numbered as in
+  // gemm_kernel: the m-groups of one unit share an XCD and run together, so
+  // the unit's weights stream from HBM about once for all of them
+  int s, ng, mg;
+  if (g.m_groups > 1) {
+    const int q = (int)(blockIdx.x >> 3);
+    const int unit = (q / g.m_groups) * 8 + (int)(blockIdx.x & 7);
+    if (unit >= g.n_groups * g.nsplit) return;   // the whole workgroup, before any barrier
+    mg = q % g.m_groups;
+    s = unit % g.nsplit;
+    ng = unit / g.nsplit;
+  } else {
+    s = (int)blockIdx.x % g.nsplit;
+    ng = (int)blockIdx.x / g.nsplit;
+    mg = 0;
+  }
+  const int mt0 = mg * 8;
   const int tile0 = (int)((long)ng * g.W.n_tiles / g.n_groups);
   const int nt = (int)((long)(ng + 1) * g.W.n_tiles / g.n_groups) - tile0;
   const int wt0 = tile0 + (ts * nt) / 2;   // this wave's tiles: [wt0, wt0 + wnt), wnt <= NTW
@@ -918,7 +933,7 @@ __global__ __launch_bounds__(256, 1) void wide_kernel(GemmArgs g, EpiArgs e) {
     const int f = wave * DPW + d;
     if (f < XF || f >= FR) {
       const int fx = f < XF ? f : 0;
-      const int mt = min(fx % MT, g.X.mtiles - 1);
+      const int mt = min(mt0 + fx % MT, g.X.mtiles - 1);
       dsrc[d] = (const uint8_t*)(fx / MT ? g.X.lo : g.X.hi);
       doff[d] = (uint32_t)(((size_t)mt * g.X.nkb + kbA) * BLOCK_BYTES + lane * FRAG_BYTES);
     } else {
@@ -992,7 +1007,7 @@ __global__ __launch_bounds__(256, 1) void wide_kernel(GemmArgs g, EpiArgs e) {
     if (t >= wnt) continue;   // uniform over the wave
 #pragma unroll
     for (int m = 0; m < MPW; ++m)
-      epilogue_tile<T, EPI_PART>(e, s, wt0 + t, mp * MPW + m, acc[t][m], lane, 1.f, nullptr);
+      epilogue_tile<T, EPI_PART>(e, s, wt0 + t, mt0 + mp * MPW + m, acc[t][m], lane, 1.f, nullptr);
   }
 }
 
@@ -1005,15 +1020,17 @@ inline hipError_t launch_wide(const GemmPlan& p, GemmArgs g, const EpiArgs& e, h
     g.nsplit = p.nsplit;
     g.n_groups = p.n_groups;
     g.m_groups = p.m_groups;
-    // one m-group; every tile in a range of at most 2 * ntg tiles (ntg per
-    // wave slot); direct-load offsets within 32 bits; every split non-empty
+    // every tile in a range of at most 2 * ntg tiles (ntg per wave slot);
+    // direct-load offsets within 32 bits; every split non-empty
     const size_t wbytes = (size_t)g.W.n_tiles * g.W.nkb * BLOCK_BYTES;
     const size_t xbytes = (size_t)g.X.mtiles * g.X.nkb * BLOCK_BYTES;
-    if (!p.split || !g.X.lo || p.m_groups != 1 || g.X.mtiles < 1 || g.X.nkb < g.W.nkb || p.n_groups < 1 ||
+    if (!p.split || !g.X.lo || p.m_groups < 1 || g.X.mtiles < 1 || g.X.nkb < g.W.nkb || p.n_groups < 1 ||
         (g.W.n_tiles + p.n_groups - 1) / p.n_groups > 2 * p.ntg || wbytes >= (1ull << 32) ||
         xbytes >= (1ull << 32) || (size_t)(p.nsplit - 1) * p.kbu >= (size_t)g.W.nkb)
       return hipErrorInvalidValue;
-    const dim3 grid((unsigned)p.n_groups * p.nsplit);
+    // several m-groups: units padded to a multiple of 8 (see the kernel)
+    const unsigned units = (unsigned)p.n_groups * p.nsplit;
+    const dim3 grid(p.m_groups > 1 ? (units + 7u) / 8u * 8u * (unsigned)p.m_groups : units);
     switch (p.ntg) {
       case 2: hipLaunchKernelGGL((wide_kernel<T, 2>), grid, dim3(256), 0, s, g, e); break;
       case 3: hipLaunchKernelGGL((wide_kernel<T, 3>), grid, dim3(256), 0, s, g, e); break;
