@@ -15,8 +15,9 @@ namespace dflash {
 // loses bandwidth; measured on the Qwen3-4B-shaped phases on MI355X.
 constexpr int kCUs = 256;
 // wide_kernel takes the split-K products of five to WIDE_MAX_MTILES m-tiles
-// (one or two 128-row m-groups: K = 80-128 at batch 1, 256 rows at batch 16)
-constexpr int WIDE_MAX_MTILES = 16;
+// (one to eight 128-row m-groups: K = 80-1024 at batch 1, 256 rows at batch
+// 16, verification of up to 1024 rows)
+constexpr int WIDE_MAX_MTILES = 64;
 
 // tiles-per-workgroup variants compiled for each m-tile count, and the
 // largest one used: with many activation rows a workgroup re-reads every row
@@ -92,15 +93,16 @@ GemmPlan plan_gemm(int epi, const Packed& W, int M, bool split_ok, bool rowmajor
     p.m_groups = (mtiles + 3) / 4;
   }
   const int T = W.n_tiles;
-  // One or two 128-row m-groups with the hi/lo pair: the split-K product
+  // One to eight 128-row m-groups with the hi/lo pair: the split-K product
   // (EPI_PART, the output and down projections above four m-tiles) runs
   // wide_kernel, eight tiles per workgroup (four per wave slot), with about
   // one round of workgroups over its tile groups and m-groups and splits of
   // at least eight k-blocks.  Measured at the Qwen3-4B shape, per launch: o
   // + down average 21.1 -> 16.2 us at 128 rows (down 29 -> about 22 us with
-  // 12 splits), 36.7 -> 23.5 us at 256 rows (batch 16); gate/up on
-  // wide_kernel was no faster than gemm_kernel in 64-row groups (46.2 vs
-  // 46.3 us at 128 rows), so it stays there.
+  // 12 splits), 36.7 -> 23.5 us at 256 rows (batch 16); per block at 1024
+  // rows o 0.44 -> 0.30 ms and down 0.94 -> 0.66 ms.  Gate/up on wide_kernel
+  // was no faster than gemm_kernel in 64-row groups (46.2 vs 46.3 us at 128
+  // rows), so it stays there.
   if (p.split && mtiles > 4 && mtiles <= WIDE_MAX_MTILES && epi == EPI_PART && !rowmajor) {
     p.wide = true;
     p.mtt = 8;
