@@ -184,16 +184,34 @@ __device__ __forceinline__ uint32_t argmax_index(unsigned long long key) {
   return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
 }
 
-__device__ __forceinline__ float wave_xor_max16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one
+// MFMA output column).  v_permlane16_swap / v_permlane32_swap applied to two
+// copies of v leave, in every lane, v and the value of lane l ^ 16 (l ^ 32)
+// as the pair: VALU instructions, where a shuffle (ds_bpermute) runs in the
+// LDS pipeline and its wait also waits for every LDS read issued before it.
+// Same results as the shuffles, bit for bit (max, and sums of two terms).
+__device__ __forceinline__ float xor16_max(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
-__device__ __forceinline__ float wave_xor_sum16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float xor32_max(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
+__device__ __forceinline__ float xor16_sum(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float wave_xor_max16_32(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float wave_xor_sum16_32(float v) { return xor32_sum(xor16_sum(v)); }
 
 // Per-sequence device descriptor of the proposer state.
 struct DevSeq {
