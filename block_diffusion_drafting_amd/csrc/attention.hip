@@ -286,15 +286,15 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
             sv[j][e] = (key < cend && key <= key_lim[j]) ? sv[j][e] : -INFINITY;
           }
         }
-        float mx = -INFINITY;
+        float mx = sv[j][0];
 #pragma unroll
-        for (int e = 0; e < NV; ++e) mx = fmaxf(mx, sv[j][e]);
+        for (int e = 1; e < NV; ++e) mx = fmax_ieee(mx, sv[j][e]);
         mx = wave_xor_max16_32(mx) * sc;
         // lazy rescaling and the hardware 2^x (as in attention_mq_kernel):
         // the reference moves only when a column's maximum exceeds it by
         // more than 8 (log2 units)
         if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
-          const float m_new = fmaxf(m_run[j], mx);
+          const float m_new = fmax_ieee(m_run[j], mx);
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
           l_run[j] *= alpha;
 #pragma unroll
@@ -563,7 +563,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
             sv[e] = (kk < lim && c0 + kk <= key_lim[j]) ? sv[e] : -INFINITY;
           }
         }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmax_ieee(mx, sv[e]);
         mx = wave_xor_max16_32(mx) * sc;
         // Lazy rescaling: the reference m_run moves (and O and l are
         // rescaled) only when some column's maximum exceeds it by more than
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         // O / l is the same for any reference; the merge of the splits
         // takes (m, l, O) with any reference.
         if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
-          const float m_new = fmaxf(m_run[j], mx);
+          const float m_new = fmax_ieee(m_run[j], mx);
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);
           l_run[j] *= alpha;
 #pragma unroll

@@ -184,21 +184,27 @@ __device__ __forceinline__ uint32_t argmax_index(unsigned long long key) {
   return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
 }
 
+// IEEE 754-2019 maximum (a NaN operand gives NaN): one v_maximum3_f32 for
+// up to three operands.  fmaxf (maxNum) needs its operands quieted first in
+// the default IEEE mode, one more VALU instruction per operand that is not
+// the result of arithmetic (an MFMA result, a lane exchange).
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one
 // MFMA output column).  v_permlane16_swap / v_permlane32_swap applied to two
 // copies of v leave, in every lane, v and the value of lane l ^ 16 (l ^ 32)
 // as the pair: VALU instructions, where a shuffle (ds_bpermute) runs in the
 // LDS pipeline and its wait also waits for every LDS read issued before it.
-// Same results as the shuffles, bit for bit (max, and sums of two terms).
+// Same results as the shuffles, bit for bit (maxima, and sums of two terms).
 __device__ __forceinline__ float xor16_max(float v) {
   const unsigned u = __float_as_uint(v);
   const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return fmax_ieee(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float xor32_max(float v) {
   const unsigned u = __float_as_uint(v);
   const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return fmax_ieee(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float xor16_sum(float v) {
   const unsigned u = __float_as_uint(v);
