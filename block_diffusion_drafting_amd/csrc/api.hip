@@ -1003,7 +1003,7 @@ static dflash_status draft_impl(dflash_ctx* c, const int32_t* ids, int K, int32_
     if (wgs <= round_wgs || chunk >= max_len + K) break;
   }
   const int max_splits = splits(max_len, chunk);
-  if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d) * sizeof(float))))
+  if ((st = ensure(c->alloc, c->attn_part, attn_part_floats(B, nkv, qgroups, max_splits, d, attn_part_o_bytes(ces, qgroups, d)) * sizeof(float))))
     return st;
 
   if (!fused.embedded) {

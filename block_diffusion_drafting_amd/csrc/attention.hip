@@ -42,9 +42,44 @@ namespace dflash {
 template <typename T, int D>
 constexpr int chunk_keys() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
 
-size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d) {
-  // per wave: O^T [d][16] + m[16] + l[16]
-  return (size_t)B * nkv * qgroups * max_splits * 4 * (d * 16 + 32);
+// Split partials, per (sequence, KV head, query group, split, wave): O^T / l
+// of the wave's 16 query columns (d x 16, in the MFMA accumulator layout:
+// lane l, d tile t holds four values at element (t * 64 + l) * 4), then
+// m[16] and l[16] in fp32.  O / l is a convex combination of V rows, so
+// |O / l| is at most the largest |V|.  The four-query-group kernel keeps it
+// in fp16 (its V is fp16; 11 significant bits against the 8 of the bf16
+// output the merge writes), halving the traffic of its large partials; the
+// register-staged kernel, whose few partials are merged at the latency of a
+// round trip either way, keeps fp32 (PB: bytes per element of O / l).
+template <int PB, int D>
+constexpr int part_wave_floats() { return D * 16 * PB / 4 + 32; }
+
+size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d, int part_o_bytes) {
+  const size_t wave = (size_t)d * 16 * part_o_bytes / 4 + 32;
+  return (size_t)B * nkv * qgroups * max_splits * 4 * wave;
+}
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// d tile t of a wave's partial: this lane's four values of O^T, times inv
+// (1 / l of the lane's query column)
+template <int PB>
+__device__ __forceinline__ void store_part_o(float* pp, int t, int lane, f32x4 o, float inv) {
+  if constexpr (PB == 2) {
+    const f16x4 h = {(_Float16)(o[0] * inv), (_Float16)(o[1] * inv), (_Float16)(o[2] * inv), (_Float16)(o[3] * inv)};
+    *(u32x2*)((uint8_t*)pp + (size_t)(t * 64 + lane) * 8) = __builtin_bit_cast(u32x2, h);
+  } else {
+    *(f32x4*)(pp + (t * 64 + lane) * 4) = o * inv;
+  }
+}
+template <int PB>
+__device__ __forceinline__ f32x4 load_part_o(const float* pp, int t, int lane) {
+  if constexpr (PB == 2) {
+    const f16x4 h = __builtin_bit_cast(f16x4, gld((const u32x2*)((const uint8_t*)pp + (size_t)(t * 64 + lane) * 8)));
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else {
+    return gld((const f32x4*)(pp + (t * 64 + lane) * 4));
+  }
 }
 
 // 16-byte nontemporal (streaming) global load.
@@ -365,20 +400,21 @@ __global__ __launch_bounds__(256 * QG) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
   // o[j][t][e] = O^T[d = 16t + 4*g4 + e][query column col] of tile j; every
-  // split writes its partial (m, l, O); attn_combine merges them in split
-  // order.  Padding query groups (past the count) write nothing.
-  const size_t wstride = (size_t)D * 16 + 32;
+  // split writes its partial (m, l, O / l); attn_combine merges them in
+  // split order.  Padding query groups (past the count) write nothing.
+  constexpr int PB = 4, WF = part_wave_floats<PB, D>(), MO = WF - 32;
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const float l_sum = wave_xor_sum16_32(l_run[j]);
     if (qg[j] >= a.qgroups) continue;
     const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg[j];
-    float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
+    float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * (size_t)WF;
+    const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;   // (no key seen: l = 0, m = -inf)
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) *(f32x4*)(pp + (t * 64 + lane) * 4) = o[j][t];
+    for (int t = 0; t < NDT; ++t) store_part_o<PB>(pp, t, lane, o[j][t], inv);
     if (g4 == 0) {
-      pp[D * 16 + col] = m_run[j];
-      pp[D * 16 + 16 + col] = l_sum;
+      pp[MO + col] = m_run[j];
+      pp[MO + 16 + col] = l_sum;
     }
   }
 }
@@ -650,18 +686,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
   wait_vm<0>();   // (none outstanding: the last chunk waited for all)
 
-  const size_t wstride = (size_t)D * 16 + 32;
+  constexpr int PB = 2, WF = part_wave_floats<PB, D>(), MO = WF - 32;
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const float l_sum = wave_xor_sum16_32(l_run[j]);
     if (qg[j] >= a.qgroups) continue;   // padding query group
     const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg[j];
-    float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * wstride;
+    float* pp = a.part + ((unit * a.max_splits + s) * 4 + wave) * (size_t)WF;
+    const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;   // (no key seen: l = 0, m = -inf)
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) *(f32x4*)(pp + (t * 64 + lane) * 4) = o[j][t];
+    for (int t = 0; t < NDT; ++t) store_part_o<PB>(pp, t, lane, o[j][t], inv);
     if (g4 == 0) {
-      pp[D * 16 + col] = m_run[j];
-      pp[D * 16 + 16 + col] = l_sum;
+      pp[MO + col] = m_run[j];
+      pp[MO + 16 + col] = l_sum;
     }
   }
 }
@@ -673,7 +710,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
 // waves, no LDS merge) when there are at most eight.  Writes its part of o
 // (frag layout of the model type T over nq*d, input of the output
 // projection).
-template <typename T, int D, int Q>
+template <typename T, int D, int Q, int PB>
 __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag out) {
   constexpr int NDT = D / 16;
   constexpr int BATCH = 8;
@@ -695,21 +732,24 @@ __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag 
   const int per = (n_s + Q - 1) / Q;
   const int s_begin = min(n_s, quarter * per), s_end = min(n_s, s_begin + per);
   const size_t unit = ((size_t)b * a.nkv + g) * a.qgroups + qg;
-  const size_t wstride = (size_t)D * 16 + 32;
-  const float* base = a.part + (unit * a.max_splits * 4 + qt) * wstride;
-  const size_t sstride = 4 * wstride;   // next split, same query tile
+  constexpr int WF = part_wave_floats<PB, D>(), MO = WF - 32;
+  const float* base = a.part + (unit * a.max_splits * 4 + qt) * (size_t)WF;
+  const size_t sstride = 4 * (size_t)WF;   // next split, same query tile
   float M = -INFINITY, L = 0.f;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = s_begin; s0 < s_end; s0 += BATCH) {
+    // (loads under a branch: the compiler waits for each split's before the
+    // next split's, and yet measured faster than a batch of unconditional
+    // loads that re-read the last split for the indices past the end)
     float ms[BATCH], ls[BATCH];
     f32x4 os[BATCH];
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       if (s0 + k < s_end) {
         const float* pp = base + (s0 + k) * sstride;
-        ms[k] = gld(pp + D * 16 + col);
-        ls[k] = gld(pp + D * 16 + 16 + col);
-        os[k] = gld((const f32x4*)(pp + (t * 64 + lane) * 4));
+        ms[k] = gld(pp + MO + col);
+        ls[k] = gld(pp + MO + 16 + col);
+        os[k] = load_part_o<PB>(pp, t, lane);   // O / l of split s0 + k
       } else {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
@@ -718,12 +758,14 @@ __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag 
     }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
+      // a split that saw no key of this column has m = -inf, l = 0, O / l = 0
       if (ms[k] == -INFINITY) continue;
       const float Mn = fmaxf(M, ms[k]);
       const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
       const float a1 = exp2f(ms[k] - Mn);
-      L = L * a0 + ls[k] * a1;
-      o = o * a0 + os[k] * a1;
+      const float w = ls[k] * a1;
+      L = L * a0 + w;
+      o = o * a0 + os[k] * w;
       M = Mn;
     }
   }
@@ -808,11 +850,14 @@ template <typename CT, typename T>
 hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s) {
   dim3 grid((unsigned)a.B * a.nkv * a.qgroups * (a.d / 16));
   const bool few = a.max_splits <= 8;   // one part: four waves per workgroup
-  switch (a.d * 2 + (few ? 1 : 0)) {
-    case 64 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 4>), grid, dim3(1024), 0, s, a, o); break;
-    case 64 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 1>), grid, dim3(256), 0, s, a, o); break;
-    case 128 * 2: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4>), grid, dim3(1024), 0, s, a, o); break;
-    case 128 * 2 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1>), grid, dim3(256), 0, s, a, o); break;
+  const int pb = attn_part_o_bytes((int)sizeof(CT), a.qgroups, a.d);
+  switch (a.d * 4 + (few ? 1 : 0) + (pb == 2 ? 2 : 0)) {
+    case 64 * 4: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 4, 4>), grid, dim3(1024), 0, s, a, o); break;
+    case 64 * 4 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 1, 4>), grid, dim3(256), 0, s, a, o); break;
+    case 128 * 4: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4, 4>), grid, dim3(1024), 0, s, a, o); break;
+    case 128 * 4 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1, 4>), grid, dim3(256), 0, s, a, o); break;
+    case 128 * 4 + 2: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4, 2>), grid, dim3(1024), 0, s, a, o); break;
+    case 128 * 4 + 3: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1, 2>), grid, dim3(256), 0, s, a, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

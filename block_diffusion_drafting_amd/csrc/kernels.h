@@ -262,13 +262,18 @@ __host__ __device__ inline void attn_split_counts(const AttnArgs& a, int ctx_len
     n_s = n_cs + (a.K + a.chunk - 1) / a.chunk;
   }
 }
-size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d);
 // Query groups (64 query rows each) per attention workgroup: one (four
 // waves), two (eight waves), or, for 2-byte operands and at least four
 // groups, four (eight waves of two query tiles each).
 inline int attn_groups_per_wg(int elem_bytes, int qgroups) {
   return qgroups >= 4 && elem_bytes == 2 ? 4 : qgroups > 1 ? 2 : 1;
 }
+// Bytes per element of O / l in the split partials: 2 (fp16) from the
+// four-query-group kernel (2-byte operands, head_dim 128), else 4 (fp32).
+inline int attn_part_o_bytes(int elem_bytes, int qgroups, int d) {
+  return elem_bytes == 2 && d == 128 && attn_groups_per_wg(elem_bytes, qgroups) == 4 ? 2 : 4;
+}
+size_t attn_part_floats(int B, int nkv, int qgroups, int max_splits, int d, int part_o_bytes);
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Merge attention splits in index order; write o (frag layout over nq*d).
