@@ -609,7 +609,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
         // as fp16 probabilities) and the rescaling, which costs more VALU
         // work than the rest of the step, is skipped once the maxima settle.
         // O / l is the same for any reference; the merge of the splits
-        // takes (m, l, O) with any reference.
+        // takes (m, l, O / l) with any reference.
         if (__ballot(mx > m_run[j] + 8.f) != 0ull) {   // wave-uniform
           const float m_new = fmax_ieee(m_run[j], mx);
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[j] - m_new);

@@ -240,7 +240,7 @@ struct AttnArgs {
   const void* bk;
   const void* bvt;
   const DevSeq* seqs;
-  float* part;            // [B][nkv][qgroups][max_splits][4 waves][d*16 + 32]
+  float* part;            // [B][nkv][qgroups][max_splits][4 waves][O / l, m, l] (attn_part_floats)
   int32_t B, K, Kpad, nq, nkv, d, layer;
   int32_t qgroups, chunk, max_splits;
   float scale_log2;
