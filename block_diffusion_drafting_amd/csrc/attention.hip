@@ -703,25 +703,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
 }
 
-// One workgroup per (sequence, KV head, query group, 16-row d-tile) with 4 Q
-// waves: wave w handles query tile 4*qg + w%4 over the part w/4 of Q of the
-// splits (its loads all issued in batches of eight), then the parts are
-// merged in order through LDS.  Q = 4 when there are many splits, 1 (four
-// waves, no LDS merge) when there are at most eight.  Writes its part of o
-// (frag layout of the model type T over nq*d, input of the output
-// projection).
-template <typename T, int D, int Q, int PB>
+// One workgroup per (sequence, KV head, query group, DT 16-row d tiles)
+// with 4 Q waves: wave w handles query tile 4*qg + w%4 over the part w/4 of
+// Q of the splits (the running max and sum of a query column are shared by
+// its d tiles), then the parts are merged in order through LDS.  Q = 4 when
+// there are many splits, 1 (four waves, no LDS merge) when there are at most
+// eight.  Writes its part of o (frag layout of the model type T over nq*d,
+// input of the output projection).
+template <typename T, int D, int Q, int PB, int DT>
 __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag out) {
-  constexpr int NDT = D / 16;
+  constexpr int NDT = D / 16, NG = NDT / DT;
+  static_assert(NDT % DT == 0, "d tiles per workgroup");
   constexpr int BATCH = 8;
   __shared__ float sm[Q][4][64], sl[Q][4][64];
-  __shared__ f32x4 so[Q][4][64];
+  __shared__ f32x4 so[Q][4][DT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qt = wave & 3, quarter = wave >> 2;
   const int g4 = lane >> 4, col = lane & 15;
   int u = blockIdx.x;
-  const int t = u % NDT;
-  u /= NDT;
+  const int t0 = (u % NG) * DT;
+  u /= NG;
   const int qg = u % a.qgroups;
   u /= a.qgroups;
   const int g = u % a.nkv;
@@ -736,24 +737,28 @@ __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag 
   const float* base = a.part + (unit * a.max_splits * 4 + qt) * (size_t)WF;
   const size_t sstride = 4 * (size_t)WF;   // next split, same query tile
   float M = -INFINITY, L = 0.f;
-  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 o[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = s_begin; s0 < s_end; s0 += BATCH) {
     // (loads under a branch: the compiler waits for each split's before the
     // next split's, and yet measured faster than a batch of unconditional
     // loads that re-read the last split for the indices past the end)
     float ms[BATCH], ls[BATCH];
-    f32x4 os[BATCH];
+    f32x4 os[BATCH][DT];
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       if (s0 + k < s_end) {
         const float* pp = base + (s0 + k) * sstride;
         ms[k] = gld(pp + MO + col);
         ls[k] = gld(pp + MO + 16 + col);
-        os[k] = load_part_o<PB>(pp, t, lane);   // O / l of split s0 + k
+#pragma unroll
+        for (int d = 0; d < DT; ++d) os[k][d] = load_part_o<PB>(pp, t0 + d, lane);   // O / l of split s0 + k
       } else {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
-        os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d = 0; d < DT; ++d) os[k][d] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
@@ -765,19 +770,22 @@ __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag 
       const float a1 = exp2f(ms[k] - Mn);
       const float w = ls[k] * a1;
       L = L * a0 + w;
-      o = o * a0 + os[k] * w;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] = o[d] * a0 + os[k][d] * w;
       M = Mn;
     }
   }
   if constexpr (Q > 1) {
     sm[quarter][qt][lane] = M;
     sl[quarter][qt][lane] = L;
-    so[quarter][qt][lane] = o;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) so[quarter][qt][d][lane] = o[d];
     __syncthreads();
     if (quarter != 0) return;
     M = -INFINITY;
     L = 0.f;
-    o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < Q; ++k) {
       const float mk = sm[k][qt][lane];
@@ -786,7 +794,8 @@ __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag 
       const float a0 = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
       const float a1 = exp2f(mk - Mn);
       L = L * a0 + sl[k][qt][lane] * a1;
-      o = o * a0 + so[k][qt][lane] * a1;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] = o[d] * a0 + so[k][qt][d][lane] * a1;
       M = Mn;
     }
   }
@@ -795,8 +804,11 @@ __global__ __launch_bounds__(256 * Q) void attn_combine_kernel(AttnArgs a, Frag 
   if (r >= a.K * rep) return;
   const int h = g * rep + r / a.K, i = r % a.K;
   const float inv = 1.f / L;
-  float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-  frag_store<T, 4>(out, b * a.K + i, h * D + t * 16 + g4 * 4, v);
+#pragma unroll
+  for (int d = 0; d < DT; ++d) {
+    float v[4] = {o[d][0] * inv, o[d][1] * inv, o[d][2] * inv, o[d][3] * inv};
+    frag_store<T, 4>(out, b * a.K + i, h * D + (t0 + d) * 16 + g4 * 4, v);
+  }
 }
 
 // (sequence, KV head, split) units padded to a multiple of 8, times the
@@ -846,18 +858,31 @@ hipError_t launch_attention(const AttnArgs& a_in, hipStream_t s) {
 template hipError_t launch_attention<f16_t>(const AttnArgs&, hipStream_t);
 template hipError_t launch_attention<float>(const AttnArgs&, hipStream_t);
 
+template <typename T, int D, int Q, int PB>
+static void launch_comb(int dt, unsigned units, hipStream_t s, const AttnArgs& a, Frag o) {
+  constexpr int NDT = D / 16;
+  if (dt == 2) hipLaunchKernelGGL((attn_combine_kernel<T, D, Q, PB, 2>), dim3(units * (NDT / 2)), dim3(256 * Q), 0, s, a, o);
+  else hipLaunchKernelGGL((attn_combine_kernel<T, D, Q, PB, 1>), dim3(units * NDT), dim3(256 * Q), 0, s, a, o);
+}
+
 template <typename CT, typename T>
 hipError_t launch_attn_combine(const AttnArgs& a, Frag o, hipStream_t s) {
-  dim3 grid((unsigned)a.B * a.nkv * a.qgroups * (a.d / 16));
+  const unsigned units = (unsigned)a.B * a.nkv * a.qgroups;
   const bool few = a.max_splits <= 8;   // one part: four waves per workgroup
   const int pb = attn_part_o_bytes((int)sizeof(CT), a.qgroups, a.d);
+  // Two d tiles per 16-wave workgroup when one per workgroup would give more
+  // workgroups than CUs: their dispatch spread over 4.3 us at K = 128 (512
+  // workgroups; merge 62 -> 52 us per block with two tiles), while a grid
+  // under one workgroup per CU is faster with one tile each (K = 16: 41
+  // against 46 us per block with two).  Four tiles spill registers.
+  const int dt = !few && units * (unsigned)(a.d / 16) > 256u ? 2 : 1;
   switch (a.d * 4 + (few ? 1 : 0) + (pb == 2 ? 2 : 0)) {
-    case 64 * 4: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 4, 4>), grid, dim3(1024), 0, s, a, o); break;
-    case 64 * 4 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 64, 1, 4>), grid, dim3(256), 0, s, a, o); break;
-    case 128 * 4: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4, 4>), grid, dim3(1024), 0, s, a, o); break;
-    case 128 * 4 + 1: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1, 4>), grid, dim3(256), 0, s, a, o); break;
-    case 128 * 4 + 2: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 4, 2>), grid, dim3(1024), 0, s, a, o); break;
-    case 128 * 4 + 3: hipLaunchKernelGGL((attn_combine_kernel<T, 128, 1, 2>), grid, dim3(256), 0, s, a, o); break;
+    case 64 * 4: launch_comb<T, 64, 4, 4>(dt, units, s, a, o); break;
+    case 64 * 4 + 1: launch_comb<T, 64, 1, 4>(1, units, s, a, o); break;
+    case 128 * 4: launch_comb<T, 128, 4, 4>(dt, units, s, a, o); break;
+    case 128 * 4 + 1: launch_comb<T, 128, 1, 4>(1, units, s, a, o); break;
+    case 128 * 4 + 2: launch_comb<T, 128, 4, 2>(dt, units, s, a, o); break;
+    case 128 * 4 + 3: launch_comb<T, 128, 1, 2>(1, units, s, a, o); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
